@@ -1,0 +1,123 @@
+"""fp64 CPU oracle for the selective state-space scan -- test infrastructure.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never imports, links or
+calls it, and it shares no code with the GPU library.
+
+The arithmetic lives in ``ssm_oracle.cpp`` (the plain sequential recurrence in
+double precision); this module only builds that file with g++ and marshals
+numpy arrays into it.  See the header of ``ssm_oracle.cpp`` for the passages of
+the pages each step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.cpp")
+_LIB_PATH = os.path.join(_HERE, "libssm_oracle.so")
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle with g++ (plain -O2, no fast-math) into ``out``."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-pthread", src, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+class Oracle:
+    """ctypes view of one build of the oracle library."""
+
+    def __init__(self, path: str = _LIB_PATH):
+        if not os.path.exists(path):
+            build(out=path)
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i64 = ctypes.c_int64
+        lib.ssm_ref_scan_f64.argtypes = [i64, i64, i64, i64, dp, dp, dp, dp, dp, dp, dp,
+                                         dp, dp, i64, ctypes.c_int, dp, dp, ctypes.c_int]
+        lib.ssm_ref_scan_f64.restype = ctypes.c_int
+        lib.ssm_ref_step_f64.argtypes = [i64, i64, i64, dp, dp, dp, dp, dp, dp, dp,
+                                         ctypes.c_int, dp, ctypes.c_int]
+        lib.ssm_ref_step_f64.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    @staticmethod
+    def _f64(a):
+        if a is None:
+            return None
+        return np.ascontiguousarray(a, dtype=np.float64)
+
+    @staticmethod
+    def _ptr(a):
+        if a is None:
+            return None
+        return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+    def scan(self, x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None,
+             zoh=False, want_h_last=True, nthreads=0):
+        """Return (y, h_last) in float64.  Shapes: x, delta (batch, L, dim);
+        A (dim, N); B, C (batch, L, N); D (dim,); h0 (batch, dim, N);
+        conv_w (dim, K); conv_b (dim,)."""
+        x, delta, A, B, C = map(self._f64, (x, delta, A, B, C))
+        D, h0, conv_w, conv_b = map(self._f64, (D, h0, conv_w, conv_b))
+        batch, L, dim = x.shape
+        N = A.shape[1]
+        assert delta.shape == x.shape and A.shape == (dim, N)
+        assert B.shape == (batch, L, N) and C.shape == (batch, L, N)
+        if D is not None:
+            assert D.shape == (dim,)
+        if h0 is not None:
+            assert h0.shape == (batch, dim, N)
+        K = 0
+        if conv_w is not None:
+            assert conv_w.ndim == 2 and conv_w.shape[0] == dim
+            K = conv_w.shape[1]
+            if conv_b is not None:
+                assert conv_b.shape == (dim,)
+        y = np.zeros((batch, L, dim), dtype=np.float64)
+        h_last = np.zeros((batch, dim, N), dtype=np.float64) if want_h_last else None
+        rc = self.lib.ssm_ref_scan_f64(batch, L, dim, N, self._ptr(x), self._ptr(delta),
+                                       self._ptr(A), self._ptr(B), self._ptr(C), self._ptr(D),
+                                       self._ptr(h0), self._ptr(conv_w), self._ptr(conv_b), K,
+                                       int(bool(zoh)), self._ptr(y), self._ptr(h_last),
+                                       int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return y, h_last
+
+    def step(self, h, x, delta, A, B, C, D=None, zoh=False, nthreads=0):
+        """One decode step.  Returns (y, h_new) in float64; ``h`` is not
+        modified.  Shapes: h (batch, dim, N); x, delta (batch, dim);
+        B, C (batch, N)."""
+        h = np.array(h, dtype=np.float64, copy=True, order="C")
+        x, delta, A, B, C, D = map(self._f64, (x, delta, A, B, C, D))
+        batch, dim, N = h.shape
+        assert x.shape == (batch, dim) and delta.shape == (batch, dim)
+        assert A.shape == (dim, N) and B.shape == (batch, N) and C.shape == (batch, N)
+        y = np.zeros((batch, dim), dtype=np.float64)
+        rc = self.lib.ssm_ref_step_f64(batch, dim, N, self._ptr(h), self._ptr(x),
+                                       self._ptr(delta), self._ptr(A), self._ptr(B),
+                                       self._ptr(C), self._ptr(D), int(bool(zoh)),
+                                       self._ptr(y), int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return y, h
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from ``ssm_oracle.cpp`` next to this file."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

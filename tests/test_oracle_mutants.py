@@ -1,0 +1,56 @@
+"""Mutation check of the oracle's pins: each test copies the oracle source,
+plants one plausible mistake (a dropped term, a wrong sign, index or operand),
+builds the copy on the CPU and requires that at least one pin rejects it.
+The real oracle is never modified."""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ssm_oracle.cpp")
+
+# (name, text in the oracle, replacement)
+MUTANTS = [
+    ("input_sign", "h[n] = abar * h[n] + bbar * u;", "h[n] = abar * h[n] - bbar * u;"),
+    ("decay_sign", "std::exp(dt * a_cont);", "std::exp(-dt * a_cont);"),
+    ("no_decay", "h[n] = abar * h[n] + bbar * u;", "h[n] = h[n] + bbar * u;"),
+    ("drop_skip", "acc + dskip * u;", "acc;"),
+    ("skip_on_x", "acc + dskip * u;", "acc + dskip * p.x[(b * L + t) * D + d];"),
+    ("zoh_no_div", "std::expm1(dt * a_cont) / a_cont;", "std::expm1(dt * a_cont);"),
+    ("zoh_sign", "std::expm1(dt * a_cont) / a_cont;", "std::expm1(-dt * a_cont) / a_cont;"),
+    ("readout_B", "acc += Ct[n] * h[n];", "acc += Bt[n] * h[n];"),
+    ("readout_before_update",
+     "h[n] = abar * h[n] + bbar * u;\n      acc += Ct[n] * h[n];",
+     "acc += Ct[n] * h[n];\n      h[n] = abar * h[n] + bbar * u;"),
+    ("delta_lag", "const double dt = p.delta[(b * L + t) * D + d];",
+     "const double dt = p.delta[(b * L + (t > 0 ? t - 1 : 0)) * D + d];"),
+    ("A_transposed", "const double a_cont = p.A[d * N + n];",
+     "const double a_cont = p.A[(n * D + d) % (D * N)];"),
+    ("conv_flipped", "const int64_t src = t - (K - 1) + k;", "const int64_t src = t - k;"),
+    ("conv_no_bias", "double z = p.conv_b ? p.conv_b[d] : 0.0;", "double z = 0.0;"),
+    ("silu_sign", "return z / (1.0 + std::exp(-z));", "return z / (1.0 + std::exp(z));"),
+    ("ignore_h0", "h[n] = p.h0 ? p.h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;"),
+    ("B_lag", "const double* Bt = p.Bm + (b * L + t) * N;",
+     "const double* Bt = p.Bm + (b * L + (t > 0 ? t - 1 : 0)) * N;"),
+    ("C_from_batch0", "const double* Ct = p.Cm + (b * L + t) * N;",
+     "const double* Ct = p.Cm + t * N;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_reject_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site not unique: %s" % name
+    mut_src = tmp_path / ("oracle_%s.cpp" % name)
+    mut_src.write_text(src.replace(old, new))
+    lib = oracle.build(src=str(mut_src), out=str(tmp_path / ("lib_%s.so" % name)))
+    orc = oracle.Oracle(lib)
+    failures = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError as e:
+            failures.append(pin.__name__)
+    assert failures, "no pin caught mutant %s" % name
