@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Throughput of the selective-scan forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fp32]
+
+A step is one ssm_scan_fwd call over the whole workload (every pass of the
+hot path: chunk summaries, carry combine, output pass) on inputs already
+resident in HBM.  W untimed steps, then exactly K timed steps between two
+device synchronizations.  Prints one JSON line.
+
+The default workload is the fp32 scan batch=8, L=2048, D=1536, N=16 (x, B,
+C ~ N(0,1), Delta log-uniform in [1e-3, 0.1], A_log[d,n] = log(n+1),
+D_skip ~ U(0.5, 1.5)).  The decode workload times 512 consecutive ssm_step
+calls as one step.
+
+Roofline of the dominant kernel (the output pass k_scan_out): its duration is
+measured per launch with HIP events that the library records around that
+kernel on the launch stream.  Two roofs are evaluated:
+  hbm  algorithmic bytes of the call / duration vs 8000 GB/s;
+  alu  algorithmic VALU lane-slots / duration vs 256 CU x 4 SIMD x 16 lanes
+       x 2.4 GHz = 39.3 T lane-slots/s, where an element costs 6 slots for
+       Delta*B (v_mul, v_exp at half rate = 2, v_mul, v_fma, v_fma) or 8 for
+       ZOH, plus 2 slots per (b, t, d) (Delta*u and the skip term).
+The reported bound is the roof with the higher utilisation.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "scan elems (B·L·D·N)/s and achieved HBM GB/s vs MI355X peak, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+SLOT_PEAK = 256 * 4 * 16 * 2.4e9          # VALU lane-slots per second
+KERNEL_SRC = os.path.join(ROOT, "selective_state_space_83_amd", "csrc", "ssm_kernels.hpp")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# HIP events through the runtime's C API (for the library's event hooks)
+# ---------------------------------------------------------------------------
+
+class HipEvents:
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError("hipEventCreate failed: %d" % rc)
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        self.hip.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work
+# ---------------------------------------------------------------------------
+
+def algorithmic_bytes(w, h0=False, h_last=False) -> int:
+    s_in = 2 if w.in_dtype == "bf16" else 4
+    s_out = 2 if w.out_dtype == "bf16" else 4
+    Bt, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
+    n = Bt * L * (D * (2 * s_in + s_out) + N * 2 * s_in) + 4 * D * N + 4 * D
+    if w.conv_k:
+        n += 4 * D * w.conv_k + 4 * D
+    n += 4 * Bt * D * N * (int(h0) + int(h_last))
+    return n
+
+
+def algorithmic_slots(w) -> float:
+    per_elem = 8.0 if w.zoh else 6.0
+    per_btd = 2.0
+    if w.conv_k:
+        per_btd += 4 + 2 + 2 + 2   # 4 taps, exp (2), rcp (2), add + mul of SiLU
+    Bt, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
+    return Bt * L * D * (N * per_elem + per_btd)
+
+
+def traffic_record(workload: str):
+    """HBM traffic of k_scan_out from committed rocprofv3 --pmc summaries,
+    valid only if the kernel source is unchanged since they were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_k_scan_out_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# runs
+# ---------------------------------------------------------------------------
+
+def to_dev(a, dtype, torch):
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.cuda()
+
+
+def bench_scan(w, steps, warmup, torch, ssm, chunk_len=0):
+    import ssm_inputs as SI
+    inp = SI.scan_inputs(w)
+    t = {k: to_dev(inp[k], w.in_dtype, torch) for k in ("x", "delta", "B", "C")}
+    for k in ("A", "D", "conv_w", "conv_b"):
+        t[k] = to_dev(inp[k], "f32", torch)
+    odt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
+    y = torch.empty(t["x"].shape, dtype=odt, device="cuda")
+    args = ssm.make_scan_args(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], y=y,
+                              conv_w=t["conv_w"], conv_b=t["conv_b"], zoh=w.zoh,
+                              chunk_len=chunk_len)
+    ws_bytes = ssm.workspace_size(args)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    chunk = ssm.plan_chunk_len(args)
+    hip = HipEvents()
+    evs = hip.create(2 * steps)
+    stream = torch.cuda.current_stream()
+
+    def call(i=None):
+        ev = (evs[2 * i], evs[2 * i + 1]) if i is not None else None
+        ssm.scan(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], conv_w=t["conv_w"],
+                 conv_b=t["conv_b"], zoh=w.zoh, y=y, want_h_last=False, workspace=ws,
+                 events=ev, stream=stream, chunk_len=chunk_len)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = e0.elapsed_time(e1)
+    out_ms = [hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)]
+    hip.destroy(evs)
+
+    # the same call with L2/MALL flushed before each one (events around the call only)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    fl = []
+    for _ in range(min(steps, 20)):
+        flush.fill_(1)
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        call()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        fl.append(a0.elapsed_time(a1))
+    del flush
+    return dict(inp=inp, total_ms=total_ms, wall_s=wall, out_ms=out_ms, flushed_ms=fl,
+                chunk_len=chunk, chunks=-(-w.seqlen // chunk), workspace=ws_bytes)
+
+
+def bench_decode(w, steps, warmup, torch, ssm):
+    """One step = `w.steps` consecutive ssm_step calls."""
+    import ssm_inputs as SI
+    n = w.steps
+    inp = SI.decode_inputs(w)
+    h = to_dev(inp["h"], "f32", torch)
+    A, Dv = to_dev(inp["A"], "f32", torch), to_dev(inp["D"], "f32", torch)
+    xs, ds_, Bs, Cs = (to_dev(inp[k], w.in_dtype, torch) for k in ("x", "delta", "B", "C"))
+    y = torch.empty((w.batch, w.dim), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        for s in range(n):
+            ssm.step(h, xs[s], ds_[s], A, Bs[s], Cs[s], Dv, y=y)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return dict(total_ms=e0.elapsed_time(e1), wall_s=time.perf_counter() - t0)
+
+
+def cpu_baseline(w, inp, budget_s=20.0):
+    """The oracle, untuned, on this host's cores: whole batch rows of the same
+    workload, as many as fit the CPU budget (at least one)."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    orc = oracle.default()
+    # time one batch row first, then scale the sample to the budget
+    rows = 1
+    t0 = time.perf_counter()
+    orc.scan(inp["x"][:1], inp["delta"][:1], inp["A"], inp["B"][:1], inp["C"][:1], inp["D"],
+             conv_w=inp.get("conv_w"), conv_b=inp.get("conv_b"), zoh=w.zoh,
+             want_h_last=False, nthreads=cores)
+    dt = time.perf_counter() - t0
+    elems = w.seqlen * w.dim * w.dstate
+    extra = int(min(w.batch - 1, max(0, budget_s / max(dt, 1e-6) - 1)))
+    if extra > 0:
+        t1 = time.perf_counter()
+        orc.scan(inp["x"][1:1 + extra], inp["delta"][1:1 + extra], inp["A"],
+                 inp["B"][1:1 + extra], inp["C"][1:1 + extra], inp["D"],
+                 conv_w=inp.get("conv_w"), conv_b=inp.get("conv_b"), zoh=w.zoh,
+                 want_h_last=False, nthreads=cores)
+        dt += time.perf_counter() - t1
+        rows += extra
+    return {"value": rows * elems / dt, "unit": "elem/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d batch rows (%d x %d x %d elems each), fp64 sequential "
+                      "recurrence, %.1f s wall" % (rows, w.batch, w.seqlen, w.dim, w.dstate, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="fp32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk-len", type=int, default=0,
+                    help="force the scan's chunk length (0 = the library's plan)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the scan is not sharded across GPUs in this "
+              "library (see the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_83_amd as ssm
+    import ssm_inputs as SI
+
+    ssm.load_library()
+    w = SI.WORKLOADS[args.workload]
+    torch.cuda.init()
+    log("bench: workload %s, %d warmup + %d timed steps" % (w, args.warmup, args.steps))
+
+    if w.steps:
+        r = bench_decode(w, args.steps, args.warmup, torch, ssm)
+        ms = r["total_ms"] / args.steps
+        elems = w.elems
+        bytes_ = w.steps * (2 * 4 * w.batch * w.dim * w.dstate
+                            + w.batch * w.dim * 6 + w.batch * w.dstate * 4) \
+            + 4 * w.dim * (w.dstate + 1)
+        out = {"metric": METRIC, "value": elems / (ms * 1e-3), "unit": "elem/s", "n_gpus": 1,
+               "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+               "dtype": "f32", "data": "synthetic",
+               "config": {"workload": "decode", "batch": w.batch, "dim": w.dim,
+                          "dstate": w.dstate, "tokens_per_step": w.steps,
+                          "in_dtype": w.in_dtype, "state": "f32"},
+               "hbm_gbps": bytes_ / (ms * 1e-3) / 1e9,
+               "roofline": None, "cpu_baseline": None}
+        print(json.dumps(out), flush=True)
+        return
+
+    r = bench_scan(w, args.steps, args.warmup, torch, ssm, args.chunk_len)
+    ms = r["total_ms"] / args.steps
+    elems = w.elems
+    out_us = float(np.mean(r["out_ms"])) * 1e3
+    abytes = algorithmic_bytes(w)
+    slots = algorithmic_slots(w)
+    hbm_ach = abytes / (out_us * 1e-6) / 1e9
+    alu_ach = slots / (out_us * 1e-6) / 1e12
+    hbm_frac = hbm_ach / HBM_PEAK_GBS
+    alu_frac = alu_ach / (SLOT_PEAK / 1e12)
+    traffic = traffic_record(w.name)
+    if alu_frac > hbm_frac:
+        roof = {"bound": "alu", "achieved": alu_ach, "peak": SLOT_PEAK / 1e12,
+                "unit": "T lane-slot/s", "frac": alu_frac, "traffic": traffic}
+    else:
+        roof = {"bound": "hbm", "achieved": hbm_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": hbm_frac, "traffic": traffic}
+    roof["kernel"] = "k_scan_out"
+    roof["kernel_us"] = out_us
+    roof["hbm_view"] = {"achieved_gbps": hbm_ach, "frac": hbm_frac}
+    roof["alu_view"] = {"achieved_tslots": alu_ach, "frac": alu_frac}
+    whole_gbps = abytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on the host")
+        cpu = cpu_baseline(w, r["inp"])
+    dtype = "f32"   # arithmetic and state are fp32 for every storage dtype
+    out = {"metric": METRIC, "value": elems / (ms * 1e-3), "unit": "elem/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": dtype, "data": "synthetic",
+           "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
+                      "dstate": w.dstate, "in_dtype": w.in_dtype, "out_dtype": w.out_dtype,
+                      "disc": "zoh" if w.zoh else "delta_b", "conv_k": w.conv_k,
+                      "chunk_len": r["chunk_len"], "chunks": r["chunks"]},
+           "hbm_gbps": whole_gbps, "hbm_frac": whole_gbps / HBM_PEAK_GBS,
+           "flushed_ms_per_step": float(np.median(r["flushed_ms"])),
+           "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * ssm_scan.h -- C ABI of libssmscan.so, the selective state-space scan
+ * (Mamba's S6 layer core) for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For every batch row b, channel d and state n the library
+ * runs one diagonal single-input single-output state-space model:
+ *
+ *   Abar_t[n] = exp(Delta[b,t,d] * A[d,n])
+ *   Bbar_t[n] = Delta[b,t,d] * B[b,t,n]                       (SSM_DISC_DELTA_B)
+ *             = (exp(Delta[b,t,d] A[d,n]) - 1) / A[d,n] * B[b,t,n]   (SSM_DISC_ZOH)
+ *   h_t[n]    = Abar_t[n] * h_{t-1}[n] + Bbar_t[n] * u[b,t,d]
+ *   y[b,t,d]  = sum_n C[b,t,n] * h_t[n] + Dskip[d] * u[b,t,d]
+ *
+ * with h_{-1} = h0 (zero when h0 is NULL) and u the scan input: x itself, or
+ * the causal depthwise conv1d + SiLU of x when conv_w is given,
+ *
+ *   u[b,t,d] = silu(conv_b[d] + sum_{k<K} conv_w[d,k] * x[b, t-K+1+k, d]),
+ *   x[b, t<0, d] = 0,   silu(z) = z / (1 + exp(-z)).
+ *
+ * Passages defining each step (web pages on Mamba; section names as printed):
+ *   - continuous SSM, ZOH discretization Abar = exp(Delta A),
+ *     Bbar = (Delta A)^-1 (exp(Delta A) - I) Delta B, and the discrete
+ *     recurrence h_k = Abar h_{k-1} + Bbar x_k, y_k = C h_k + D x_k:
+ *     gsyq.cn "Mamba 状态空间模型深度解析", section "连续到离散的转换";
+ *   - the simplified Bbar = Delta * B and the scan h = associative_scan(
+ *     A_bar, B_bar * x), y = C * h: same page, section "硬件优化并行扫描算法";
+ *   - A kept continuous and discretized on the fly; one independent SSM per
+ *     channel with A (D, N), B and C (batch, L, N), Delta (batch, L, D); C is
+ *     a 1 x N row, so the readout contracts over n: VMamba reading note,
+ *     sections "离散化SSM", "S4中三个矩阵的维度表示、维度变化" and
+ *     "mamba：从S4到S6的算法变化流程";
+ *   - the causal depthwise Conv1d (padding d_conv - 1, groups = d_model) before
+ *     the SSM and the skip D * x_conv on the conv output: gsyq.cn section
+ *     "选择性的实现细节" (SelectiveSSM);
+ *   - the single-token recurrent step with a cached state (constant cost per
+ *     generated token): 53ai.com explainer, section "一、Motivation", and the
+ *     datacamp tutorial's complexity table.
+ *
+ * Conventions shared by every entry point.
+ *   Layout     all arrays are dense, row-major, last dimension fastest:
+ *              x, Delta, y (batch, L, D); B, C (batch, L, N); A (D, N);
+ *              Dskip, conv_b (D); conv_w (D, K); h0, h_last (batch, D, N).
+ *              Base pointers must be aligned to their element size; B and C
+ *              rows are read with scalar loads, so B and C base pointers must
+ *              be 4-byte aligned and are best 64-byte aligned.
+ *   Memory     every pointer is a DEVICE pointer owned by the caller.  The
+ *              library allocates nothing, keeps no pointer after the call and
+ *              holds no global mutable state; it is reentrant and thread-safe.
+ *   Streams    hip_stream is a hipStream_t (NULL = the default stream).  Work
+ *              is enqueued asynchronously; the call never synchronizes.
+ *   Errors     all argument checks run on the host before anything is
+ *              enqueued; on any error the outputs are untouched and the
+ *              status says why (ssm_last_error_message() has the detail).  A
+ *              failed launch returns SSM_ERR_HIP; faults inside kernels
+ *              surface at the caller's next synchronization.
+ *   Dtypes     x, Delta, B, C share in_dtype (fp32 or bf16); y has out_dtype;
+ *              A, Dskip, conv weights and states are fp32; arithmetic and the
+ *              state are fp32; bf16 outputs are rounded to nearest even.
+ *   Empty      seqlen == 0 or batch * dim == 0 is valid.  With seqlen == 0 and
+ *              batch * dim > 0, h_last (if given) receives h0 (zeros if h0 is
+ *              NULL) and nothing else is touched.
+ */
+#ifndef SSM_SCAN_H_
+#define SSM_SCAN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL = 1,        /* a required pointer (or the args struct) is NULL */
+  SSM_ERR_SHAPE = 2,       /* negative sizes, or byte counts overflow int64 */
+  SSM_ERR_DTYPE = 3,       /* unknown dtype or discretization enum value */
+  SSM_ERR_UNSUPPORTED = 4, /* dstate not in {1,2,4,8,16}, conv_k not in 1..4,
+                              misaligned pointer, negative chunk_len */
+  SSM_ERR_ALIAS = 5,       /* an output overlaps an input or another output */
+  SSM_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
+  SSM_ERR_HIP = 7          /* the HIP runtime rejected a launch */
+} ssm_status_t;
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+
+typedef enum { SSM_DISC_DELTA_B = 0, SSM_DISC_ZOH = 1 } ssm_disc_t;
+
+typedef struct {
+  int64_t batch, seqlen, dim, dstate; /* Bt, L, D, N */
+  int32_t in_dtype;                   /* ssm_dtype_t of x, delta, Bm, Cm */
+  int32_t out_dtype;                  /* ssm_dtype_t of y */
+  int32_t disc;                       /* ssm_disc_t */
+  int32_t conv_k;                     /* taps of the conv prologue (1..4); ignored if conv_w is NULL */
+  const void* x;                      /* (Bt, L, D) */
+  const void* delta;                  /* (Bt, L, D), the step size, already positive */
+  const float* A;                     /* (D, N), continuous-time diagonal */
+  const void* Bm;                     /* (Bt, L, N) */
+  const void* Cm;                     /* (Bt, L, N) */
+  const float* Dskip;                 /* (D) or NULL = no skip term */
+  const float* h0;                    /* (Bt, D, N) or NULL = zero initial state */
+  float* h_last;                      /* (Bt, D, N) or NULL: state after the last token */
+  void* y;                            /* (Bt, L, D) output */
+  const float* conv_w;                /* (D, K) or NULL = no conv prologue */
+  const float* conv_b;                /* (D) or NULL = zero bias */
+  void* workspace;                    /* device scratch of >= ssm_scan_workspace_size() bytes */
+  size_t workspace_bytes;
+  int32_t chunk_len;                  /* time steps per chunk; 0 = library's choice */
+  int32_t reserved;                   /* must be 0 */
+  void* ev_main_start;                /* optional hipEvent_t recorded on hip_stream right */
+  void* ev_main_stop;                 /* before / after the output-pass kernel; NULL = none */
+} ssm_scan_args_t;
+
+typedef struct {
+  int64_t batch, dim, dstate;         /* Bt, D, N */
+  int32_t in_dtype;                   /* ssm_dtype_t of x, delta, Bm, Cm */
+  int32_t out_dtype;                  /* ssm_dtype_t of y */
+  int32_t disc;                       /* ssm_disc_t */
+  int32_t reserved;                   /* must be 0 */
+  const void* x;                      /* (Bt, D) the new token's scan input */
+  const void* delta;                  /* (Bt, D) */
+  const float* A;                     /* (D, N) */
+  const void* Bm;                     /* (Bt, N) */
+  const void* Cm;                     /* (Bt, N) */
+  const float* Dskip;                 /* (D) or NULL */
+  float* h;                           /* (Bt, D, N) cached state, updated in place */
+  void* y;                            /* (Bt, D) output, read from the updated state */
+} ssm_step_args_t;
+
+/* Returns SSM_ABI_VERSION. */
+int ssm_abi_version(void);
+
+/* Bytes of device workspace ssm_scan_fwd needs for these arguments (0 when the
+ * plan scans each sequence in one piece).  Reads only the sizes, chunk_len and
+ * dtypes; pure host function, no HIP call.  Returns 0 for invalid sizes. */
+size_t ssm_scan_workspace_size(const ssm_scan_args_t* args);
+
+/* Time steps per chunk the plan uses for these arguments (equal to seqlen
+ * when the scan is not split).  Pure host function; 0 for invalid sizes. */
+int64_t ssm_scan_plan_chunk_len(const ssm_scan_args_t* args);
+
+/* Selective-scan forward: y and (optionally) h_last from the inputs above.
+ * The time axis may be split into chunks scanned in parallel; their carries
+ * are combined with the associative operator
+ *   (a, b) o (a', b') = (a a', a' b + b')
+ * which is exact up to floating-point rounding order. */
+ssm_status_t ssm_scan_fwd(const ssm_scan_args_t* args, void* hip_stream);
+
+/* One recurrent decode step per sequence: h <- Abar h + Bbar x, then
+ * y = C . h + Dskip * x, with h updated in place.  Same arithmetic as
+ * ssm_scan_fwd with seqlen = 1, h0 = h_last = h and no conv prologue.
+ * y must not overlap h or any input. */
+ssm_status_t ssm_step(const ssm_step_args_t* args, void* hip_stream);
+
+/* Static description of a status code. */
+const char* ssm_status_string(ssm_status_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* ssm_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H_ */

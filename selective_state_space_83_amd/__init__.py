@@ -1,0 +1,292 @@
+"""selective_state_space_83_amd -- the selective state-space scan (the core of
+Mamba's S6 layer) on AMD Instinct MI355X.
+
+This module is a thin ctypes binding over ``libssmscan.so`` (contract:
+``include/ssm_scan.h``).  It only checks tensor placement and marshals
+pointers, sizes and the current HIP stream; every step of the computation runs
+in the library's HIP kernels.  PyTorch supplies device memory and streams.
+
+    y, h_last = scan(x, delta, A, B, C, D=None, h0=None, ...)
+    y = step(h, x, delta, A, B, C, D=None, ...)      # h updated in place
+
+Shapes: x, delta (batch, L, dim); A (dim, N); B, C (batch, L, N); D (dim,);
+h0, h_last, h (batch, dim, N); conv_w (dim, K <= 4); conv_b (dim,).
+x, delta, B, C are float32 or bfloat16 (all the same); A, D, states and conv
+weights are float32.
+
+If the library is not built, importing works but every call raises: there is
+no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssmscan.so")
+
+SSM_OK = 0
+SSM_ERR_NULL = 1
+SSM_ERR_SHAPE = 2
+SSM_ERR_DTYPE = 3
+SSM_ERR_UNSUPPORTED = 4
+SSM_ERR_ALIAS = 5
+SSM_ERR_WORKSPACE = 6
+SSM_ERR_HIP = 7
+
+SSM_F32 = 0
+SSM_BF16 = 1
+SSM_DISC_DELTA_B = 0
+SSM_DISC_ZOH = 1
+
+
+class ScanArgs(ctypes.Structure):
+    """Mirror of ssm_scan_args_t."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+        ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("disc", ctypes.c_int32), ("conv_k", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("delta", ctypes.c_void_p), ("A", ctypes.c_void_p),
+        ("Bm", ctypes.c_void_p), ("Cm", ctypes.c_void_p), ("Dskip", ctypes.c_void_p),
+        ("h0", ctypes.c_void_p), ("h_last", ctypes.c_void_p), ("y", ctypes.c_void_p),
+        ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("chunk_len", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("ev_main_start", ctypes.c_void_p), ("ev_main_stop", ctypes.c_void_p),
+    ]
+
+
+class StepArgs(ctypes.Structure):
+    """Mirror of ssm_step_args_t."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("disc", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("delta", ctypes.c_void_p), ("A", ctypes.c_void_p),
+        ("Bm", ctypes.c_void_p), ("Cm", ctypes.c_void_p), ("Dskip", ctypes.c_void_p),
+        ("h", ctypes.c_void_p), ("y", ctypes.c_void_p),
+    ]
+
+
+EXPORTS = ["ssm_abi_version", "ssm_scan_workspace_size", "ssm_scan_plan_chunk_len",
+           "ssm_scan_fwd", "ssm_step", "ssm_status_string", "ssm_last_error_message"]
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libssmscan.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built; run __graft_entry__.build() or "
+                           "python -m selective_state_space_83_amd._build" % path)
+    lib = ctypes.CDLL(path)
+    lib.ssm_abi_version.restype = ctypes.c_int
+    lib.ssm_abi_version.argtypes = []
+    lib.ssm_scan_workspace_size.restype = ctypes.c_size_t
+    lib.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanArgs)]
+    lib.ssm_scan_plan_chunk_len.restype = ctypes.c_int64
+    lib.ssm_scan_plan_chunk_len.argtypes = [ctypes.POINTER(ScanArgs)]
+    lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), ctypes.c_void_p]
+    lib.ssm_step.restype = ctypes.c_int
+    lib.ssm_step.argtypes = [ctypes.POINTER(StepArgs), ctypes.c_void_p]
+    lib.ssm_status_string.restype = ctypes.c_char_p
+    lib.ssm_status_string.argtypes = [ctypes.c_int]
+    lib.ssm_last_error_message.restype = ctypes.c_char_p
+    lib.ssm_last_error_message.argtypes = []
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+class SSMError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__("ssm status %d: %s" % (status, detail))
+
+
+class SSMArgumentError(SSMError, ValueError):
+    pass
+
+
+def _raise_for(lib, status: int):
+    if status == SSM_OK:
+        return
+    detail = lib.ssm_last_error_message().decode() or lib.ssm_status_string(status).decode()
+    if status == SSM_ERR_HIP:
+        raise SSMError(status, detail)
+    raise SSMArgumentError(status, detail)
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers (argument marshalling only)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise ValueError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _f32(t, name):
+    torch = _torch()
+    if t is not None and t.dtype != torch.float32:
+        raise ValueError("%s must be float32" % name)
+    return t
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def make_scan_args(x, delta, A, B, C, D=None, h0=None, h_last=None, y=None, conv_w=None,
+                   conv_b=None, zoh=False, chunk_len=0) -> ScanArgs:
+    """Fill a ScanArgs from tensors (shape checks are the library's job)."""
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be (batch, L, dim) and A (dim, N)")
+    batch, L, dim = x.shape
+    a = ScanArgs()
+    a.batch, a.seqlen, a.dim, a.dstate = batch, L, dim, A.shape[1]
+    a.in_dtype = _dtype_code(x)
+    for name, t in (("delta", delta), ("B", B), ("C", C)):
+        if _dtype_code(t) != a.in_dtype:
+            raise ValueError("%s must have the dtype of x" % name)
+    if tuple(delta.shape) != tuple(x.shape):
+        raise ValueError("delta must have the shape of x")
+    if tuple(B.shape) != (batch, L, a.dstate) or tuple(C.shape) != (batch, L, a.dstate):
+        raise ValueError("B and C must be (batch, L, N)")
+    if tuple(A.shape) != (dim, a.dstate):
+        raise ValueError("A must be (dim, N)")
+    if D is not None and tuple(D.shape) != (dim,):
+        raise ValueError("D must be (dim,)")
+    for name, t in (("h0", h0), ("h_last", h_last)):
+        if t is not None and tuple(t.shape) != (batch, dim, a.dstate):
+            raise ValueError("%s must be (batch, dim, N)" % name)
+    if y is not None and tuple(y.shape) != tuple(x.shape):
+        raise ValueError("y must have the shape of x")
+    a.out_dtype = _dtype_code(y) if y is not None else a.in_dtype
+    a.disc = SSM_DISC_ZOH if zoh else SSM_DISC_DELTA_B
+    a.x, a.delta, a.A, a.Bm, a.Cm = _ptr(x), _ptr(delta), _ptr(_f32(A, "A")), _ptr(B), _ptr(C)
+    a.Dskip = _ptr(_f32(D, "D"))
+    a.h0, a.h_last = _ptr(_f32(h0, "h0")), _ptr(_f32(h_last, "h_last"))
+    a.y = _ptr(y)
+    if conv_w is not None:
+        if conv_w.dim() != 2 or conv_w.shape[0] != dim:
+            raise ValueError("conv_w must be (dim, K)")
+        if conv_b is not None and tuple(conv_b.shape) != (dim,):
+            raise ValueError("conv_b must be (dim,)")
+        a.conv_w, a.conv_b = _ptr(_f32(conv_w, "conv_w")), _ptr(_f32(conv_b, "conv_b"))
+        a.conv_k = conv_w.shape[1]
+    a.chunk_len = int(chunk_len)
+    return a
+
+
+def workspace_size(args: ScanArgs) -> int:
+    return int(load_library().ssm_scan_workspace_size(ctypes.byref(args)))
+
+
+def plan_chunk_len(args: ScanArgs) -> int:
+    return int(load_library().ssm_scan_plan_chunk_len(ctypes.byref(args)))
+
+
+def abi_version() -> int:
+    return int(load_library().ssm_abi_version())
+
+
+def scan(x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None, zoh=False,
+         out_dtype=None, want_h_last=True, y=None, h_last=None, chunk_len=0,
+         workspace=None, stream=None, events=None) -> Tuple[object, object]:
+    """Selective-scan forward on the current (or given) stream.
+
+    Returns (y, h_last); h_last is None when want_h_last is False and no
+    h_last tensor is passed.  ``workspace`` (uint8 device tensor) may be
+    passed to avoid an allocation per call; ``events`` = (start, stop) raw
+    hipEvent_t handles recorded around the output-pass kernel."""
+    torch = _torch()
+    lib = load_library()
+    if y is None:
+        odt = out_dtype if out_dtype is not None else x.dtype
+        y = torch.empty(x.shape, dtype=odt, device=x.device)
+    if h_last is None and want_h_last:
+        h_last = torch.empty((x.shape[0], x.shape[2], A.shape[1]), dtype=torch.float32,
+                             device=x.device)
+    args = make_scan_args(x, delta, A, B, C, D, h0, h_last, y, conv_w, conv_b, zoh, chunk_len)
+    need = int(lib.ssm_scan_workspace_size(ctypes.byref(args)))
+    if need > 0:
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        args.workspace = _ptr(workspace)
+        args.workspace_bytes = workspace.numel()
+    if events is not None:
+        args.ev_main_start, args.ev_main_stop = events
+    status = lib.ssm_scan_fwd(ctypes.byref(args), _stream_handle(stream))
+    _raise_for(lib, status)
+    return y, h_last
+
+
+def make_step_args(h, x, delta, A, B, C, D=None, y=None, zoh=False) -> StepArgs:
+    if h.dim() != 3 or x.dim() != 2:
+        raise ValueError("h must be (batch, dim, N) and x (batch, dim)")
+    batch, dim, N = h.shape
+    a = StepArgs()
+    a.batch, a.dim, a.dstate = batch, dim, N
+    a.in_dtype = _dtype_code(x)
+    for name, t in (("delta", delta), ("B", B), ("C", C)):
+        if _dtype_code(t) != a.in_dtype:
+            raise ValueError("%s must have the dtype of x" % name)
+    if tuple(x.shape) != (batch, dim) or tuple(delta.shape) != (batch, dim):
+        raise ValueError("x and delta must be (batch, dim)")
+    if tuple(B.shape) != (batch, N) or tuple(C.shape) != (batch, N):
+        raise ValueError("B and C must be (batch, N)")
+    if tuple(A.shape) != (dim, N):
+        raise ValueError("A must be (dim, N)")
+    if D is not None and tuple(D.shape) != (dim,):
+        raise ValueError("D must be (dim,)")
+    if y is not None and tuple(y.shape) != (batch, dim):
+        raise ValueError("y must be (batch, dim)")
+    a.out_dtype = _dtype_code(y) if y is not None else a.in_dtype
+    a.disc = SSM_DISC_ZOH if zoh else SSM_DISC_DELTA_B
+    a.x, a.delta, a.A, a.Bm, a.Cm = _ptr(x), _ptr(delta), _ptr(_f32(A, "A")), _ptr(B), _ptr(C)
+    a.Dskip = _ptr(_f32(D, "D"))
+    a.h = _ptr(_f32(h, "h"))
+    a.y = _ptr(y)
+    return a
+
+
+def step(h, x, delta, A, B, C, D=None, zoh=False, y=None, out_dtype=None, stream=None):
+    """One decode step; h (float32, (batch, dim, N)) is updated in place.
+    Returns y (batch, dim)."""
+    torch = _torch()
+    lib = load_library()
+    if y is None:
+        y = torch.empty(x.shape, dtype=out_dtype if out_dtype is not None else x.dtype,
+                        device=x.device)
+    args = make_step_args(h, x, delta, A, B, C, D, y, zoh)
+    status = lib.ssm_step(ctypes.byref(args), _stream_handle(stream))
+    _raise_for(lib, status)
+    return y

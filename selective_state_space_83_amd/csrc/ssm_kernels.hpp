@@ -1,0 +1,570 @@
+// ssm_kernels.hpp -- gfx950 device code of the selective state-space scan.
+//
+// Work decomposition (all kernels use one 64-lane wave per workgroup):
+//   * lane  = one channel (b, d); the lane keeps all N states of that channel
+//     in VGPRs for the whole chunk, so the expanded (batch, L, D, N) state is
+//     never written anywhere (the memory argument of the pages'
+//     "hardware-aware" scan: 53ai.com explainer section 3.4; VMamba note,
+//     section "硬件感知的设计");
+//   * wave  = 64 consecutive channels of one batch row and one time chunk;
+//     x, Delta, y are read/written as 64 consecutive elements per time step
+//     (one coalesced 128/256-byte row), while B[b,t,:] and C[b,t,:] are the
+//     same for every lane of the wave and are fetched with scalar loads into
+//     SGPRs, so they cost no vector-memory or VGPR bandwidth;
+//   * chunk = a slice of the time axis.  When batch * D alone does not fill the
+//     GPU, the time axis is cut into chunks scanned in parallel:
+//       k_chunk_summary  per chunk, the state reached from a zero state and
+//                        the chunk's total step sum(Delta);
+//       k_carry_combine  per (b, d, n), the carries into every chunk by the
+//                        associative operator (a, b) o (a', b') = (a a', a' b + b')
+//                        (53ai.com explainer section 3.3: split the sequence,
+//                        scan the parts, combine and adjust);
+//       k_scan_out       per chunk, the recurrence again from its carry-in,
+//                        writing y (and h_last from the final chunk).
+//     The chunk's decay factor is exp(A * sum Delta), the product of its
+//     per-step Abar factors.
+//
+// Arithmetic per element (b, t, d, n), Delta*B discretization:
+//     a = exp2(Delta * A[n] * log2 e)       v_mul + v_exp (half rate)
+//     h = a * h + (Delta * u) * B[n]        v_mul + v_fma
+//     y += C[n] * h                         v_fma
+// The ZOH discretization uses h' = a (h + q) - q with q = u B[n] / A[n], which
+// equals a h + (a - 1) q.
+//
+// Slow decay.  When |Delta A| is tiny, Abar = exp(Delta A) lies so close to 1
+// that rounding it to fp32 biases the decay rate by up to 2^-24 / |Delta A|,
+// and with a steady Delta that bias compounds over the whole memory horizon.
+// At any step where some lane has min_n |Delta A[n]| below a threshold, the
+// wave instead carries the decay as e = expm1(Delta A), evaluated by its
+// series for small arguments:  h' = h + e h + Bbar u.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssmk {
+
+using bf16_t = uint16_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWave = 64;
+constexpr int kConvTaps = 4;   // the conv prologue always runs 4 taps; shorter
+                               // filters are zero-padded at the oldest taps
+
+enum Disc : int { kDeltaB = 0, kZoh = 1 };
+
+struct ScanParams {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const float* h0;
+  float* h_last;
+  void* y;
+  const float* conv_w;   // (D, conv_k)
+  const float* conv_b;
+  float* dsum;           // (Bt, C-1, D)       chunk sums of Delta
+  float* hsum;           // (Bt, C-1, D, N)    chunk end states, then carries
+  int64_t Bt, L, D;
+  int64_t T;             // chunk length
+  int64_t C;             // number of chunks
+  int32_t dtiles;        // ceil(D / 64)
+  int32_t conv_k;
+  int32_t nwg;           // workgroups in the launch (for the XCD remap)
+  float exact_thr;       // min |Delta A| below this takes the slow-decay form
+};
+
+struct StepParams {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  float* h;
+  void* y;
+  int64_t Bt, D;
+  int32_t dtiles;
+  int32_t nwg;
+  float exact_thr;
+};
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float ld(const float* p) { return *p; }
+__device__ __forceinline__ float ld(const bf16_t* p) {
+  return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+}
+
+__device__ __forceinline__ void st(float* p, float v) { *p = v; }
+__device__ __forceinline__ void st(bf16_t* p, float v) {
+  // round to nearest even (gfx950 has a native conversion for this)
+  *p = __builtin_bit_cast(bf16_t, static_cast<__bf16>(v));
+}
+
+// Rows of B and C are identical across the wave: fetch them through the
+// constant address space so the compiler emits scalar loads into SGPRs.
+typedef const float __attribute__((address_space(4)))* const_f32_ptr;
+typedef const uint32_t __attribute__((address_space(4)))* const_u32_ptr;
+
+template <int N>
+__device__ __forceinline__ void load_row(float (&r)[N], const float* p) {
+  const_f32_ptr q = (const_f32_ptr)(p);
+#pragma unroll
+  for (int n = 0; n < N; ++n) r[n] = q[n];
+}
+
+template <int N>
+__device__ __forceinline__ void load_row(float (&r)[N], const bf16_t* p) {
+  if constexpr (N == 1) {
+    // a single bf16 per row: a 16-bit vector load (a dword scalar load could
+    // run 2 bytes past the end of the array)
+    r[0] = ld(p);
+  } else {
+    const_u32_ptr q = (const_u32_ptr)(p);
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) {
+      const uint32_t w = q[k];
+      r[2 * k] = __uint_as_float(w << 16);
+      r[2 * k + 1] = __uint_as_float(w & 0xffff0000u);
+    }
+  }
+}
+
+__device__ __forceinline__ float exp2_fast(float v) { return __builtin_amdgcn_exp2f(v); }
+
+__device__ __forceinline__ float silu(float z) {
+  // z / (1 + exp(-z)); for z -> -inf the exp overflows to inf and rcp gives 0
+  const float e = exp2_fast(-z * kLog2e);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Workgroups are handed to the 8 XCDs round-robin (id i on XCD i % 8).  Map
+// them so that each XCD receives one contiguous range of logical ids, which
+// keeps the waves sharing a (batch, chunk) -- and its B/C rows -- in one L2.
+__device__ __forceinline__ int xcd_remap(int i, int nwg) {
+  const int x = i & 7, k = i >> 3;
+  const int q = nwg >> 3, r = nwg & 7;
+  return x * q + (x < r ? x : r) + k;
+}
+
+// Per-lane constants of one channel.
+template <int N, int DISC>
+struct ChanConst {
+  float A2[N];     // A[d,n] * log2(e)
+  float invA[N];   // 1 / A[d,n] (0 where A is 0); ZOH only
+  float thr;       // Delta below thr means some |Delta A[n]| is below the threshold
+};
+
+template <int N, int DISC>
+__device__ __forceinline__ void load_chan(ChanConst<N, DISC>& cc, const float* A, int64_t d,
+                                          float thr_scale) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const float a = A[d * N + n];
+    cc.A2[n] = a * kLog2e;
+    if constexpr (DISC == kZoh) cc.invA[n] = (a != 0.0f) ? 1.0f / a : 0.0f;
+    amax = fmaxf(amax, (a != 0.0f) ? 1.0f / fabsf(a) : __builtin_inff());
+  }
+  // min_n |Delta A[n]| < thr_scale  <=>  Delta < thr_scale * max_n 1/|A[n]|
+  cc.thr = thr_scale * amax;
+}
+
+// expm1(z) given z2 = z * log2(e) and a = exp2(z2): the series
+// z (1 + z/2 + z^2/6 + z^3/24 + z^4/120) below |z| = 1/16 (truncation error
+// under 4e-11 relative), a - 1 above it (relative error under ~1e-6 there).
+__device__ __forceinline__ float expm1_from(float z2, float a) {
+  const float z = z2 * kLn2;
+  float p = fmaf(z, 1.0f / 120.0f, 1.0f / 24.0f);
+  p = fmaf(z, p, 1.0f / 6.0f);
+  p = fmaf(z, p, 0.5f);
+  p = fmaf(z, p, 1.0f);
+  return (fabsf(z) < 0.0625f) ? z * p : a - 1.0f;
+}
+
+// One time step for one lane: updates h[] and returns sum_n C[n] h[n].
+// u is the scan input, dv = Delta.  WITH_Y = false skips the readout.
+// EXACT selects the slow-decay form (see the header).
+template <int N, int DISC, bool WITH_Y, bool EXACT>
+__device__ __forceinline__ float ssm_step_lane(float (&h)[N], const ChanConst<N, DISC>& cc,
+                                               const float (&Bv)[N], const float (&Cv)[N],
+                                               float u, float dv) {
+  float acc0 = 0.0f, acc1 = 0.0f;
+  const float du = dv * u;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const float z2 = dv * cc.A2[n];
+    const float a = exp2_fast(z2);
+    if constexpr (!EXACT) {
+      if constexpr (DISC == kDeltaB) {
+        h[n] = fmaf(a, h[n], du * Bv[n]);
+      } else {
+        const float q = (u * Bv[n]) * cc.invA[n];
+        h[n] = fmaf(a, h[n] + q, -q);
+      }
+    } else {
+      const float e = expm1_from(z2, a);
+      float gu;   // the input factor times u
+      if constexpr (DISC == kDeltaB) {
+        gu = du;
+      } else {
+        gu = (cc.invA[n] != 0.0f) ? (e * cc.invA[n]) * u : du;   // A = 0: limit Delta
+      }
+      h[n] = fmaf(e, h[n], fmaf(gu, Bv[n], h[n]));
+    }
+    if constexpr (WITH_Y) {
+      if (n & 1) acc1 = fmaf(Cv[n], h[n], acc1);
+      else acc0 = fmaf(Cv[n], h[n], acc0);
+    }
+  }
+  return acc0 + acc1;
+}
+
+template <int N, int DISC, bool WITH_Y>
+__device__ __forceinline__ float ssm_step_any(float (&h)[N], const ChanConst<N, DISC>& cc,
+                                              const float (&Bv)[N], const float (&Cv)[N],
+                                              float u, float dv) {
+  // wave-uniform choice: the fast form unless some lane has a tiny |Delta A|
+  if (__builtin_amdgcn_ballot_w64(dv < cc.thr) != 0)
+    return ssm_step_lane<N, DISC, WITH_Y, true>(h, cc, Bv, Cv, u, dv);
+  return ssm_step_lane<N, DISC, WITH_Y, false>(h, cc, Bv, Cv, u, dv);
+}
+
+// Causal conv window: taps w[0..3] (oldest .. newest, zero-padded at the
+// oldest end for K < 4) and the previous three inputs.
+struct ConvState {
+  float w0, w1, w2, w3, bias;
+  float xm3, xm2, xm1;   // x[t-3], x[t-2], x[t-1]
+};
+
+template <typename InT>
+__device__ __forceinline__ void conv_init(ConvState& cs, const ScanParams& p, int64_t b,
+                                          int64_t d, int64_t t0) {
+  const int K = p.conv_k;
+  float w[kConvTaps] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < K; ++k) w[kConvTaps - K + k] = p.conv_w[d * K + k];
+  cs.w0 = w[0]; cs.w1 = w[1]; cs.w2 = w[2]; cs.w3 = w[3];
+  cs.bias = p.conv_b ? p.conv_b[d] : 0.0f;
+  const InT* xp = static_cast<const InT*>(p.x);
+  const int64_t base = b * p.L;
+  cs.xm3 = (t0 >= 3) ? ld(xp + (base + t0 - 3) * p.D + d) : 0.0f;
+  cs.xm2 = (t0 >= 2) ? ld(xp + (base + t0 - 2) * p.D + d) : 0.0f;
+  cs.xm1 = (t0 >= 1) ? ld(xp + (base + t0 - 1) * p.D + d) : 0.0f;
+}
+
+__device__ __forceinline__ float conv_push(ConvState& cs, float xv) {
+  float z = fmaf(cs.w3, xv, cs.bias);
+  z = fmaf(cs.w2, cs.xm1, z);
+  z = fmaf(cs.w1, cs.xm2, z);
+  z = fmaf(cs.w0, cs.xm3, z);
+  cs.xm3 = cs.xm2; cs.xm2 = cs.xm1; cs.xm1 = xv;
+  return silu(z);
+}
+
+// Lane offset within a 64-channel tile, clamped so that lanes past the last
+// channel duplicate channel D - 1.
+__device__ __forceinline__ uint32_t lane_offset(int64_t dbase, int64_t D) {
+  const int64_t last = D - 1 - dbase;
+  const uint32_t l = threadIdx.x;
+  return (static_cast<int64_t>(l) <= last) ? l : static_cast<uint32_t>(last);
+}
+
+// Decompose a (remapped) workgroup id of the chunked grid.
+struct Tile {
+  int64_t b, chunk, dtile;
+};
+
+__device__ __forceinline__ Tile tile_of(int wg, int64_t dtiles, int64_t nchunks) {
+  Tile t;
+  t.dtile = wg % dtiles;
+  const int64_t r = wg / dtiles;
+  t.chunk = r % nchunks;
+  t.b = r / nchunks;
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// the time loop shared by the summary and output passes
+// ---------------------------------------------------------------------------
+
+constexpr int kUnroll = 8;   // time steps whose x / Delta loads are batched
+
+// Vector access at a wave-uniform base plus a 32-bit per-lane byte offset:
+// lets the compiler use the SGPR-base + VGPR-offset addressing form, so no
+// per-lane 64-bit address arithmetic is spent on the streams.
+template <typename T>
+__device__ __forceinline__ float ldo(const T* base, uint32_t byte_off) {
+  return ld(reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off));
+}
+template <typename T>
+__device__ __forceinline__ void sto(T* base, uint32_t byte_off, float v) {
+  st(reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off), v);
+}
+
+// Lanes past the last channel (D not a multiple of 64) run channel D - 1
+// again: they read the same inputs and produce bit-identical results, so all
+// stores can be unconditional (duplicate stores of equal values to one
+// address) and no branch splits the wave.
+//
+// Scalar-load schedule: the B and C rows of step t + 1 are requested at the
+// top of step t into the second of two row buffers, so a whole step of
+// arithmetic covers their latency.  (Scalar loads complete out of order, so
+// the only usable wait is "all outstanding"; it falls at the top of the next
+// step, after the loads had a full step to land.)
+template <int N, typename InT, typename OutT, int DISC, bool CONV, bool OUT>
+__device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64_t dbase,
+                                           uint32_t lo, int64_t t0, int32_t steps, float (&h)[N],
+                                           float* dsum_out) {
+  const int64_t d = dbase + lo;
+  ChanConst<N, DISC> cc;
+  load_chan<N, DISC>(cc, p.A, d, p.exact_thr);
+  const float dsk = (OUT && p.Dskip) ? p.Dskip[d] : 0.0f;
+  ConvState cs;
+  if constexpr (CONV) conv_init<InT>(cs, p, b, d, t0);
+
+  const int64_t D = p.D;
+  const uint32_t lo_in = lo * sizeof(InT);
+  const uint32_t lo_out = lo * sizeof(OutT);
+  const InT* xrow = static_cast<const InT*>(p.x) + (b * p.L + t0) * D + dbase;
+  const InT* drow = static_cast<const InT*>(p.delta) + (b * p.L + t0) * D + dbase;
+  const InT* Brow = static_cast<const InT*>(p.Bm) + (b * p.L + t0) * N;
+  const InT* Crow = static_cast<const InT*>(p.Cm) + (b * p.L + t0) * N;
+  OutT* yrow = OUT ? static_cast<OutT*>(p.y) + (b * p.L + t0) * D + dbase : nullptr;
+
+  float dacc = 0.0f;
+  if (steps <= 0) return;
+
+  // Two row buffers used in turn (no register copies): step j computes with
+  // buffer j & 1 and fetches the next step's rows into buffer (j + 1) & 1.
+  float Bb0[N], Bb1[N], Cb0[N], Cb1[N];
+  load_row<N>(Bb0, Brow);
+  if constexpr (OUT) load_row<N>(Cb0, Crow);
+
+  auto one_step = [&](float xv, float dv, bool has_next, float (&Bcur)[N], float (&Bnext)[N],
+                      float (&Ccur)[N], float (&Cnext)[N]) {
+    // on the last step re-read the current row instead of running past the end
+    const int64_t adv = has_next ? N : 0;
+    load_row<N>(Bnext, Brow + adv);
+    if constexpr (OUT) load_row<N>(Cnext, Crow + adv);
+    const float u = CONV ? conv_push(cs, xv) : xv;
+    if constexpr (OUT) {
+      const float acc = ssm_step_any<N, DISC, true>(h, cc, Bcur, Ccur, u, dv);
+      sto(yrow, lo_out, fmaf(dsk, u, acc));
+      yrow += D;
+    } else {
+      ssm_step_any<N, DISC, false>(h, cc, Bcur, Bcur, u, dv);
+    }
+    Brow += N;
+    Crow += N;
+  };
+
+  // The chunk's sum of Delta feeds exp(A * sum) in the carry combine, so it
+  // is kept accurate: block sums of kUnroll steps are added with Kahan
+  // compensation (a plain running fp32 sum of a steady Delta drifts by
+  // ~length * 2^-25 relative, which the decay amplifies by |A * sum|).
+  float dcomp = 0.0f;
+  auto sum_add = [&](float v) {
+    const float yv = v - dcomp;
+    const float tv = dacc + yv;
+    dcomp = (tv - dacc) - yv;
+    dacc = tv;
+  };
+
+  static_assert(kUnroll % 2 == 0, "row buffers alternate within a block");
+  const int32_t nblk = steps / kUnroll;
+  float xc[kUnroll], dc[kUnroll];
+  if (nblk > 0) {
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      xc[j] = ldo(xrow + j * D, lo_in);
+      dc[j] = ldo(drow + j * D, lo_in);
+    }
+  }
+  for (int32_t blk = 0; blk < nblk; ++blk) {
+    float xn[kUnroll], dn[kUnroll];
+    const bool more = blk + 1 < nblk;
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        xn[j] = ldo(xrow + (kUnroll + j) * D, lo_in);
+        dn[j] = ldo(drow + (kUnroll + j) * D, lo_in);
+      }
+    }
+    const int32_t tb = blk * kUnroll;
+#pragma unroll
+    for (int j = 0; j < kUnroll; j += 2) {
+      one_step(xc[j], dc[j], tb + j + 1 < steps, Bb0, Bb1, Cb0, Cb1);
+      one_step(xc[j + 1], dc[j + 1], tb + j + 2 < steps, Bb1, Bb0, Cb1, Cb0);
+    }
+    if constexpr (!OUT) {
+      float bs = dc[0];
+#pragma unroll
+      for (int j = 1; j < kUnroll; ++j) bs += dc[j];
+      sum_add(bs);
+    }
+    xrow += kUnroll * D;
+    drow += kUnroll * D;
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) { xc[j] = xn[j]; dc[j] = dn[j]; }
+    }
+  }
+  // remainder (fewer than kUnroll steps); the current rows are in Bb0 / Cb0
+  for (int32_t t = nblk * kUnroll; t < steps; ++t) {
+    const float xv = ldo(xrow, lo_in);
+    const float dv = ldo(drow, lo_in);
+    one_step(xv, dv, t + 1 < steps, Bb0, Bb1, Cb0, Cb1);
+    if constexpr (!OUT) sum_add(dv);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      Bb0[n] = Bb1[n];
+      if constexpr (OUT) Cb0[n] = Cb1[n];
+    }
+    xrow += D;
+    drow += D;
+  }
+  if (!OUT && dsum_out) *dsum_out = dacc - dcomp;
+}
+
+// ---------------------------------------------------------------------------
+// kernels
+// ---------------------------------------------------------------------------
+
+// Pass 1 (chunked plans): for chunks 0..C-2, the state each chunk reaches from
+// a zero state, and its sum of Delta.
+template <int N, typename InT, int DISC, bool CONV>
+__global__ void __launch_bounds__(kWave) k_chunk_summary(const ScanParams p) {
+  const int wg = xcd_remap(blockIdx.x, p.nwg);
+  const Tile tl = tile_of(wg, p.dtiles, p.C - 1);
+  const int64_t dbase = tl.dtile * kWave;
+  const uint32_t lo = lane_offset(dbase, p.D);
+  const int64_t d = dbase + lo;
+  const int64_t t0 = tl.chunk * p.T;
+  const int32_t steps = static_cast<int32_t>(p.T);   // chunks before the last are full
+  float h[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) h[n] = 0.0f;
+  const int64_t slot = tl.b * (p.C - 1) + tl.chunk;
+  chunk_loop<N, InT, float, DISC, CONV, false>(p, tl.b, dbase, lo, t0, steps, h,
+                                               p.dsum + slot * p.D + d);
+  float* hs = p.hsum + (slot * p.D + d) * N;
+#pragma unroll
+  for (int n = 0; n < N; ++n) hs[n] = h[n];
+}
+
+// exp(z) * carry + b with z2 = z * log2(e), keeping the decay accurate when
+// exp(z) is close to 1 (carry + expm1(z) carry + b).
+__device__ __forceinline__ float decay_add(float z2, float carry, float b) {
+  return fmaf(expm1_from(z2, exp2_fast(z2)), carry, carry + b);
+}
+
+// Pass 2: carries.  One lane per (b, d, n); walks the chunks in order,
+//   carry_0 = h0,  carry_{c+1} = exp(A * sum_c Delta) * carry_c + hsum_c,
+// and overwrites hsum_c with carry_{c+1}, the carry into chunk c + 1.
+template <int N>
+__global__ void __launch_bounds__(kWave) k_carry_combine(const ScanParams p) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kWave + threadIdx.x;
+  const int64_t DN = p.D * N;
+  if (idx >= p.Bt * DN) return;
+  const int64_t b = idx / DN;
+  const int64_t dn = idx - b * DN;
+  const int64_t d = dn / N;
+  const float a2 = p.A[dn] * kLog2e;
+  float carry = p.h0 ? p.h0[idx] : 0.0f;
+  const int64_t nc = p.C - 1;
+  const float* ds = p.dsum + b * nc * p.D + d;
+  float* hs = p.hsum + b * nc * DN + dn;
+  constexpr int U = 8;
+  int64_t c = 0;
+  for (; c + U <= nc; c += U) {
+    float sv[U], hv[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      sv[j] = ds[(c + j) * p.D];
+      hv[j] = hs[(c + j) * DN];
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      carry = decay_add(a2 * sv[j], carry, hv[j]);
+      hs[(c + j) * DN] = carry;
+    }
+  }
+  for (; c < nc; ++c) {
+    carry = decay_add(a2 * ds[c * p.D], carry, hs[c * DN]);
+    hs[c * DN] = carry;
+  }
+}
+
+// Pass 3 (or the only pass): scan each chunk from its carry-in, write y, and
+// h_last from the final chunk.
+template <int N, typename InT, typename OutT, int DISC, bool CONV>
+__global__ void __launch_bounds__(kWave) k_scan_out(const ScanParams p) {
+  const int wg = xcd_remap(blockIdx.x, p.nwg);
+  const Tile tl = tile_of(wg, p.dtiles, p.C);
+  const int64_t dbase = tl.dtile * kWave;
+  const uint32_t lo = lane_offset(dbase, p.D);
+  const int64_t d = dbase + lo;
+  const int64_t t0 = tl.chunk * p.T;
+  const int32_t steps = static_cast<int32_t>((t0 + p.T < p.L) ? p.T : p.L - t0);
+  float h[N];
+  if (tl.chunk == 0) {
+    if (p.h0) {
+      const float* h0 = p.h0 + (tl.b * p.D + d) * N;
+#pragma unroll
+      for (int n = 0; n < N; ++n) h[n] = h0[n];
+    } else {
+#pragma unroll
+      for (int n = 0; n < N; ++n) h[n] = 0.0f;
+    }
+  } else {
+    const float* cin = p.hsum + ((tl.b * (p.C - 1) + tl.chunk - 1) * p.D + d) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] = cin[n];
+  }
+  chunk_loop<N, InT, OutT, DISC, CONV, true>(p, tl.b, dbase, lo, t0, steps, h, nullptr);
+  if (p.h_last && tl.chunk == p.C - 1) {
+    float* hl = p.h_last + (tl.b * p.D + d) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) hl[n] = h[n];
+  }
+}
+
+// h_last for an empty sequence: a copy of h0 (or zeros).
+__global__ void __launch_bounds__(256) k_state_copy(float* dst, const float* src, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.0f;
+}
+
+// One decode step.  One lane per (b, d); b is uniform per workgroup so the B
+// and C rows are scalar loads.
+template <int N, typename InT, typename OutT, int DISC>
+__global__ void __launch_bounds__(kWave) k_step(const StepParams p) {
+  const int wg = xcd_remap(blockIdx.x, p.nwg);
+  const int64_t b = wg / p.dtiles;
+  const int64_t dtile = wg - b * p.dtiles;
+  const int64_t d = dtile * kWave + lane_offset(dtile * kWave, p.D);
+  ChanConst<N, DISC> cc;
+  load_chan<N, DISC>(cc, p.A, d, p.exact_thr);
+  float* hp = p.h + (b * p.D + d) * N;
+  float h[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) h[n] = hp[n];
+  float Bv[N], Cv[N];
+  load_row<N>(Bv, static_cast<const InT*>(p.Bm) + b * N);
+  load_row<N>(Cv, static_cast<const InT*>(p.Cm) + b * N);
+  const float u = ld(static_cast<const InT*>(p.x) + b * p.D + d);
+  const float dv = ld(static_cast<const InT*>(p.delta) + b * p.D + d);
+  const float acc = ssm_step_any<N, DISC, true>(h, cc, Bv, Cv, u, dv);
+  const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
+#pragma unroll
+  for (int n = 0; n < N; ++n) hp[n] = h[n];
+  st(static_cast<OutT*>(p.y) + b * p.D + d, fmaf(dsk, u, acc));
+}
+
+}  // namespace ssmk

@@ -1,0 +1,408 @@
+// ssm_scan.hip -- host side of libssmscan.so: argument checks, the chunk plan,
+// template dispatch and kernel launches.  The device code is ssm_kernels.hpp;
+// the public contract is include/ssm_scan.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "ssm_scan.h"
+#include "ssm_kernels.hpp"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+ssm_status_t fail(ssm_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+// The plan targets MI355X: 256 CUs x 4 SIMDs.  A chunked plan aims at about
+// kTargetWaves waves in the output pass (three per SIMD), and never cuts chunks
+// shorter than kMinChunk steps.
+constexpr int64_t kTargetWaves = 3072;
+constexpr int64_t kMinChunk = 64;
+constexpr int64_t kChunkAlign = 8;
+constexpr int64_t kMaxChunk = int64_t(1) << 30;   // kernels count steps in 32 bits
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+
+size_t dtype_size(int32_t dt) { return dt == SSM_BF16 ? 2 : 4; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool supported_n(int64_t n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; }
+
+struct Plan {
+  int64_t T = 0;       // chunk length
+  int64_t C = 0;       // chunks
+  int64_t dtiles = 0;  // ceil(D / 64)
+  size_t ws_dsum = 0;  // bytes
+  size_t ws_hsum = 0;
+  size_t ws_total = 0;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Sizes are assumed validated (non-negative, no overflow).
+Plan make_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t chunk_len) {
+  Plan pl;
+  pl.dtiles = (D + ssmk::kWave - 1) / ssmk::kWave;
+  if (L == 0 || Bt * D == 0) return pl;
+  int64_t T;
+  if (chunk_len > 0) {
+    T = std::min<int64_t>(chunk_len, L);
+  } else {
+    const int64_t waves = Bt * pl.dtiles;
+    int64_t C = (kTargetWaves + waves - 1) / waves;
+    C = std::max<int64_t>(1, std::min<int64_t>(C, L / kMinChunk));
+    T = (L + C - 1) / C;
+    if (C > 1) T = (T + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+    T = std::min(T, L);
+  }
+  pl.T = std::min(T, kMaxChunk);
+  pl.C = (L + pl.T - 1) / pl.T;
+  if (pl.C > 1) {
+    pl.ws_dsum = align256(size_t(Bt) * size_t(pl.C - 1) * size_t(D) * 4);
+    pl.ws_hsum = align256(size_t(Bt) * size_t(pl.C - 1) * size_t(D) * size_t(N) * 4);
+    pl.ws_total = pl.ws_dsum + pl.ws_hsum;
+  }
+  return pl;
+}
+
+struct Range {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+bool misaligned(const void* p, size_t align) {
+  return p && (reinterpret_cast<uintptr_t>(p) % align) != 0;
+}
+
+// Validation common to the scan; fills the plan on success.
+ssm_status_t check_scan(const ssm_scan_args_t* a, Plan* plan) {
+  if (!a) return fail(SSM_ERR_NULL, "args is NULL");
+  if (a->batch < 0 || a->seqlen < 0 || a->dim < 0)
+    return fail(SSM_ERR_SHAPE, "negative size: batch=%lld seqlen=%lld dim=%lld",
+                (long long)a->batch, (long long)a->seqlen, (long long)a->dim);
+  if (a->dstate < 1) return fail(SSM_ERR_SHAPE, "dstate must be >= 1 (got %lld)", (long long)a->dstate);
+  if (a->in_dtype != SSM_F32 && a->in_dtype != SSM_BF16)
+    return fail(SSM_ERR_DTYPE, "unknown in_dtype %d", a->in_dtype);
+  if (a->out_dtype != SSM_F32 && a->out_dtype != SSM_BF16)
+    return fail(SSM_ERR_DTYPE, "unknown out_dtype %d", a->out_dtype);
+  if (a->disc != SSM_DISC_DELTA_B && a->disc != SSM_DISC_ZOH)
+    return fail(SSM_ERR_DTYPE, "unknown discretization %d", a->disc);
+  if (!supported_n(a->dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not in {1,2,4,8,16}", (long long)a->dstate);
+  if (a->conv_w && (a->conv_k < 1 || a->conv_k > ssmk::kConvTaps))
+    return fail(SSM_ERR_UNSUPPORTED, "conv_k %d not in 1..4", a->conv_k);
+  if (a->chunk_len < 0) return fail(SSM_ERR_UNSUPPORTED, "chunk_len must be >= 0");
+  if (a->reserved != 0) return fail(SSM_ERR_UNSUPPORTED, "reserved field must be 0");
+  // byte counts must fit in int64 (and the grid in a launch)
+  int64_t bl, bld, bln, dn, bdn;
+  if (!mul_ok(a->batch, a->seqlen, &bl) || !mul_ok(bl, a->dim, &bld) ||
+      !mul_ok(bl, a->dstate, &bln) || !mul_ok(a->dim, a->dstate, &dn) ||
+      !mul_ok(a->batch, dn, &bdn) || bld > INT64_MAX / 8 || bln > INT64_MAX / 8 ||
+      bdn > INT64_MAX / 8)
+    return fail(SSM_ERR_SHAPE, "sizes overflow");
+  *plan = make_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len);
+  if (a->seqlen == 0 || a->batch * a->dim == 0) {
+    // only h_last may be written (with h0 or zeros)
+    if (a->batch * a->dim > 0 && a->h_last && a->h0 &&
+        overlap({a->h_last, size_t(bdn) * 4}, {a->h0, size_t(bdn) * 4}))
+      return fail(SSM_ERR_ALIAS, "h_last overlaps h0");
+    return SSM_OK;
+  }
+  if (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->y)
+    return fail(SSM_ERR_NULL, "x, delta, A, Bm, Cm and y are required");
+  const size_t in_sz = dtype_size(a->in_dtype), out_sz = dtype_size(a->out_dtype);
+  if (misaligned(a->x, in_sz) || misaligned(a->delta, in_sz) || misaligned(a->Bm, 4) ||
+      misaligned(a->Cm, 4) || misaligned(a->y, out_sz) || misaligned(a->A, 4) ||
+      misaligned(a->Dskip, 4) || misaligned(a->h0, 4) || misaligned(a->h_last, 4) ||
+      misaligned(a->conv_w, 4) || misaligned(a->conv_b, 4) || misaligned(a->workspace, 256))
+    return fail(SSM_ERR_UNSUPPORTED,
+                "misaligned pointer (element alignment; B, C 4 bytes; workspace 256 bytes)");
+  const Range y{a->y, size_t(bld) * out_sz};
+  const Range hl{a->h_last, size_t(bdn) * 4};
+  const Range ins[] = {
+      {a->x, size_t(bld) * in_sz},        {a->delta, size_t(bld) * in_sz},
+      {a->A, size_t(dn) * 4},             {a->Bm, size_t(bln) * in_sz},
+      {a->Cm, size_t(bln) * in_sz},       {a->Dskip, size_t(a->dim) * 4},
+      {a->h0, size_t(bdn) * 4},           {a->conv_w, size_t(a->dim) * size_t(std::max(a->conv_k, 0)) * 4},
+      {a->conv_b, a->conv_w ? size_t(a->dim) * 4 : 0},
+  };
+  for (const Range& r : ins) {
+    if (overlap(y, r)) return fail(SSM_ERR_ALIAS, "y overlaps an input");
+    if (overlap(hl, r)) return fail(SSM_ERR_ALIAS, "h_last overlaps an input");
+  }
+  if (overlap(y, hl)) return fail(SSM_ERR_ALIAS, "y overlaps h_last");
+  if (plan->ws_total > 0) {
+    if (!a->workspace) return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required", plan->ws_total);
+    if (a->workspace_bytes < plan->ws_total)
+      return fail(SSM_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", a->workspace_bytes,
+                  plan->ws_total);
+    const Range ws{a->workspace, plan->ws_total};
+    for (const Range& r : ins)
+      if (overlap(ws, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps an input");
+    if (overlap(ws, y) || overlap(ws, hl)) return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
+  }
+  const int64_t grid_out = a->batch * plan->C * plan->dtiles;
+  if (grid_out > kMaxGrid || (a->batch * a->dim * a->dstate + 63) / 64 > kMaxGrid)
+    return fail(SSM_ERR_SHAPE, "problem too large for one launch");
+  return SSM_OK;
+}
+
+ssm_status_t check_step(const ssm_step_args_t* a) {
+  if (!a) return fail(SSM_ERR_NULL, "args is NULL");
+  if (a->batch < 0 || a->dim < 0)
+    return fail(SSM_ERR_SHAPE, "negative size: batch=%lld dim=%lld", (long long)a->batch,
+                (long long)a->dim);
+  if (a->dstate < 1) return fail(SSM_ERR_SHAPE, "dstate must be >= 1 (got %lld)", (long long)a->dstate);
+  if (a->in_dtype != SSM_F32 && a->in_dtype != SSM_BF16)
+    return fail(SSM_ERR_DTYPE, "unknown in_dtype %d", a->in_dtype);
+  if (a->out_dtype != SSM_F32 && a->out_dtype != SSM_BF16)
+    return fail(SSM_ERR_DTYPE, "unknown out_dtype %d", a->out_dtype);
+  if (a->disc != SSM_DISC_DELTA_B && a->disc != SSM_DISC_ZOH)
+    return fail(SSM_ERR_DTYPE, "unknown discretization %d", a->disc);
+  if (!supported_n(a->dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not in {1,2,4,8,16}", (long long)a->dstate);
+  if (a->reserved != 0) return fail(SSM_ERR_UNSUPPORTED, "reserved field must be 0");
+  int64_t bd, dn, bdn, bn;
+  if (!mul_ok(a->batch, a->dim, &bd) || !mul_ok(a->dim, a->dstate, &dn) ||
+      !mul_ok(a->batch, dn, &bdn) || !mul_ok(a->batch, a->dstate, &bn) || bdn > INT64_MAX / 8)
+    return fail(SSM_ERR_SHAPE, "sizes overflow");
+  if (bd == 0) return SSM_OK;
+  if (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->h || !a->y)
+    return fail(SSM_ERR_NULL, "x, delta, A, Bm, Cm, h and y are required");
+  const size_t in_sz = dtype_size(a->in_dtype), out_sz = dtype_size(a->out_dtype);
+  if (misaligned(a->x, in_sz) || misaligned(a->delta, in_sz) || misaligned(a->Bm, 4) ||
+      misaligned(a->Cm, 4) || misaligned(a->y, out_sz) || misaligned(a->A, 4) ||
+      misaligned(a->Dskip, 4) || misaligned(a->h, 4))
+    return fail(SSM_ERR_UNSUPPORTED, "misaligned pointer (element alignment; B, C 4 bytes)");
+  const Range y{a->y, size_t(bd) * out_sz};
+  const Range h{a->h, size_t(bdn) * 4};
+  const Range ins[] = {{a->x, size_t(bd) * in_sz}, {a->delta, size_t(bd) * in_sz},
+                       {a->A, size_t(dn) * 4},     {a->Bm, size_t(bn) * in_sz},
+                       {a->Cm, size_t(bn) * in_sz}, {a->Dskip, size_t(a->dim) * 4}};
+  for (const Range& r : ins) {
+    if (overlap(y, r)) return fail(SSM_ERR_ALIAS, "y overlaps an input");
+    if (overlap(h, r)) return fail(SSM_ERR_ALIAS, "h overlaps an input");
+  }
+  if (overlap(y, h)) return fail(SSM_ERR_ALIAS, "y overlaps h");
+  if ((a->batch * ((a->dim + 63) / 64)) > kMaxGrid) return fail(SSM_ERR_SHAPE, "problem too large");
+  return SSM_OK;
+}
+
+// A step where some lane has min_n |Delta A[n]| below this threshold runs
+// the slow-decay form (expm1 of Delta A) instead of the fast one.  The fast
+// form's error is about 2^-24 / |Delta A| relative: on the decay rate for
+// Delta*B, and additionally on the input term for ZOH ((a - 1) / A).  The
+// thresholds keep that well inside the tolerance of each input precision.
+float exact_threshold(int32_t disc, int32_t in_dtype) {
+  if (disc == SSM_DISC_ZOH) return in_dtype == SSM_BF16 ? 1.0f / 8192.0f : 0.03f;
+  return in_dtype == SSM_BF16 ? 1.0f / 8192.0f : 1.0f / 1024.0f;
+}
+
+ssm_status_t launch_status(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return SSM_OK;
+}
+
+template <int N, typename InT, typename OutT, int DISC, bool CONV>
+ssm_status_t run_scan(ssmk::ScanParams kp, const Plan& pl, hipStream_t s, hipEvent_t ev0,
+                      hipEvent_t ev1) {
+  if (pl.C > 1) {
+    kp.nwg = int32_t(kp.Bt * (pl.C - 1) * pl.dtiles);
+    hipLaunchKernelGGL((ssmk::k_chunk_summary<N, InT, DISC, CONV>), dim3(kp.nwg), dim3(ssmk::kWave),
+                       0, s, kp);
+    if (ssm_status_t st = launch_status("k_chunk_summary")) return st;
+    const int64_t chains = kp.Bt * kp.D * N;
+    hipLaunchKernelGGL((ssmk::k_carry_combine<N>), dim3(uint32_t((chains + 63) / 64)),
+                       dim3(ssmk::kWave), 0, s, kp);
+    if (ssm_status_t st = launch_status("k_carry_combine")) return st;
+  }
+  kp.nwg = int32_t(kp.Bt * pl.C * pl.dtiles);
+  if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return fail(SSM_ERR_HIP, "hipEventRecord failed");
+  hipLaunchKernelGGL((ssmk::k_scan_out<N, InT, OutT, DISC, CONV>), dim3(kp.nwg), dim3(ssmk::kWave), 0,
+                     s, kp);
+  if (ssm_status_t st = launch_status("k_scan_out")) return st;
+  if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return fail(SSM_ERR_HIP, "hipEventRecord failed");
+  return SSM_OK;
+}
+
+template <int N, typename InT, typename OutT>
+ssm_status_t dispatch_disc(const ssm_scan_args_t* a, const ssmk::ScanParams& kp, const Plan& pl,
+                           hipStream_t s) {
+  hipEvent_t e0 = static_cast<hipEvent_t>(a->ev_main_start);
+  hipEvent_t e1 = static_cast<hipEvent_t>(a->ev_main_stop);
+  const bool conv = a->conv_w != nullptr;
+  if (a->disc == SSM_DISC_ZOH)
+    return conv ? run_scan<N, InT, OutT, ssmk::kZoh, true>(kp, pl, s, e0, e1)
+                : run_scan<N, InT, OutT, ssmk::kZoh, false>(kp, pl, s, e0, e1);
+  return conv ? run_scan<N, InT, OutT, ssmk::kDeltaB, true>(kp, pl, s, e0, e1)
+              : run_scan<N, InT, OutT, ssmk::kDeltaB, false>(kp, pl, s, e0, e1);
+}
+
+template <int N>
+ssm_status_t dispatch_types(const ssm_scan_args_t* a, const ssmk::ScanParams& kp, const Plan& pl,
+                            hipStream_t s) {
+  using ssmk::bf16_t;
+  if (a->in_dtype == SSM_F32)
+    return a->out_dtype == SSM_F32 ? dispatch_disc<N, float, float>(a, kp, pl, s)
+                                   : dispatch_disc<N, float, bf16_t>(a, kp, pl, s);
+  return a->out_dtype == SSM_F32 ? dispatch_disc<N, bf16_t, float>(a, kp, pl, s)
+                                 : dispatch_disc<N, bf16_t, bf16_t>(a, kp, pl, s);
+}
+
+template <int N, typename InT, typename OutT>
+ssm_status_t run_step_t(const ssm_step_args_t* a, ssmk::StepParams kp, hipStream_t s) {
+  if (a->disc == SSM_DISC_ZOH)
+    hipLaunchKernelGGL((ssmk::k_step<N, InT, OutT, ssmk::kZoh>), dim3(kp.nwg), dim3(ssmk::kWave), 0,
+                       s, kp);
+  else
+    hipLaunchKernelGGL((ssmk::k_step<N, InT, OutT, ssmk::kDeltaB>), dim3(kp.nwg), dim3(ssmk::kWave),
+                       0, s, kp);
+  return launch_status("k_step");
+}
+
+template <int N>
+ssm_status_t run_step_n(const ssm_step_args_t* a, const ssmk::StepParams& kp, hipStream_t s) {
+  using ssmk::bf16_t;
+  if (a->in_dtype == SSM_F32)
+    return a->out_dtype == SSM_F32 ? run_step_t<N, float, float>(a, kp, s)
+                                   : run_step_t<N, float, bf16_t>(a, kp, s);
+  return a->out_dtype == SSM_F32 ? run_step_t<N, bf16_t, float>(a, kp, s)
+                                 : run_step_t<N, bf16_t, bf16_t>(a, kp, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+size_t ssm_scan_workspace_size(const ssm_scan_args_t* a) {
+  if (!a || a->batch < 0 || a->seqlen < 0 || a->dim < 0 || a->dstate < 1 || a->chunk_len < 0)
+    return 0;
+  int64_t bl, bld, bdn;
+  if (!mul_ok(a->batch, a->seqlen, &bl) || !mul_ok(bl, a->dim, &bld) ||
+      !mul_ok(a->batch, a->dim * a->dstate, &bdn))
+    return 0;
+  return make_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len).ws_total;
+}
+
+int64_t ssm_scan_plan_chunk_len(const ssm_scan_args_t* a) {
+  if (!a || a->batch < 0 || a->seqlen < 0 || a->dim < 0 || a->dstate < 1 || a->chunk_len < 0)
+    return 0;
+  int64_t bl, bld;
+  if (!mul_ok(a->batch, a->seqlen, &bl) || !mul_ok(bl, a->dim, &bld)) return 0;
+  return make_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len).T;
+}
+
+ssm_status_t ssm_scan_fwd(const ssm_scan_args_t* a, void* hip_stream) {
+  g_msg[0] = '\0';
+  Plan pl;
+  if (ssm_status_t st = check_scan(a, &pl)) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const int64_t BD = a->batch * a->dim;
+  if (BD == 0) return SSM_OK;
+  if (a->seqlen == 0) {
+    if (!a->h_last) return SSM_OK;
+    const int64_t n = BD * a->dstate;
+    hipLaunchKernelGGL(ssmk::k_state_copy, dim3(uint32_t((n + 255) / 256)), dim3(256), 0, s,
+                       a->h_last, a->h0, n);
+    return launch_status("k_state_copy");
+  }
+  ssmk::ScanParams kp{};
+  kp.x = a->x;
+  kp.delta = a->delta;
+  kp.A = a->A;
+  kp.Bm = a->Bm;
+  kp.Cm = a->Cm;
+  kp.Dskip = a->Dskip;
+  kp.h0 = a->h0;
+  kp.h_last = a->h_last;
+  kp.y = a->y;
+  kp.conv_w = a->conv_w;
+  kp.conv_b = a->conv_w ? a->conv_b : nullptr;
+  kp.conv_k = a->conv_w ? a->conv_k : 0;
+  kp.dsum = pl.C > 1 ? static_cast<float*>(a->workspace) : nullptr;
+  kp.hsum = pl.C > 1 ? reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pl.ws_dsum) : nullptr;
+  kp.Bt = a->batch;
+  kp.L = a->seqlen;
+  kp.D = a->dim;
+  kp.T = pl.T;
+  kp.C = pl.C;
+  kp.dtiles = int32_t(pl.dtiles);
+  kp.exact_thr = exact_threshold(a->disc, a->in_dtype);
+  switch (a->dstate) {
+    case 1: return dispatch_types<1>(a, kp, pl, s);
+    case 2: return dispatch_types<2>(a, kp, pl, s);
+    case 4: return dispatch_types<4>(a, kp, pl, s);
+    case 8: return dispatch_types<8>(a, kp, pl, s);
+    default: return dispatch_types<16>(a, kp, pl, s);
+  }
+}
+
+ssm_status_t ssm_step(const ssm_step_args_t* a, void* hip_stream) {
+  g_msg[0] = '\0';
+  if (ssm_status_t st = check_step(a)) return st;
+  if (a->batch * a->dim == 0) return SSM_OK;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  ssmk::StepParams kp{};
+  kp.x = a->x;
+  kp.delta = a->delta;
+  kp.A = a->A;
+  kp.Bm = a->Bm;
+  kp.Cm = a->Cm;
+  kp.Dskip = a->Dskip;
+  kp.h = a->h;
+  kp.y = a->y;
+  kp.Bt = a->batch;
+  kp.D = a->dim;
+  kp.dtiles = int32_t((a->dim + 63) / 64);
+  kp.nwg = int32_t(a->batch * kp.dtiles);
+  kp.exact_thr = exact_threshold(a->disc, a->in_dtype);
+  switch (a->dstate) {
+    case 1: return run_step_n<1>(a, kp, s);
+    case 2: return run_step_n<2>(a, kp, s);
+    case 4: return run_step_n<4>(a, kp, s);
+    case 8: return run_step_n<8>(a, kp, s);
+    default: return run_step_n<16>(a, kp, s);
+  }
+}
+
+const char* ssm_status_string(ssm_status_t s) {
+  switch (s) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL: return "required pointer is NULL";
+    case SSM_ERR_SHAPE: return "invalid or overflowing sizes";
+    case SSM_ERR_DTYPE: return "unknown dtype or discretization";
+    case SSM_ERR_UNSUPPORTED: return "unsupported argument";
+    case SSM_ERR_ALIAS: return "output overlaps another buffer";
+    case SSM_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSM_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* ssm_last_error_message(void) { return g_msg; }
+
+}  // extern "C"

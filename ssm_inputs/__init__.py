@@ -82,6 +82,7 @@ class Workload:
     delta_dist: str = "softplus"   # or "loguniform"
     dskip_dist: str = "one"        # or "uniform"
     steps: int = 0         # decode workloads: number of consecutive steps
+    a_dist: str = "log"    # "log": A_log[d, n] = log(n + 1); "random": -U(0.1, 8)
 
     @property
     def elems(self) -> int:
@@ -99,6 +100,9 @@ WORKLOADS = {
     "conv": Workload("conv", 3, 4, 8192, 2560, 16, "bf16", "bf16", zoh=True, conv_k=4),
     "long": Workload("long", 4, 1, 1 << 20, 512, 16, "bf16", "bf16"),
     "decode": Workload("decode", 5, 256, 1, 5120, 16, "bf16", "bf16", steps=512),
+    # carries that survive whole chunks: Delta = 1e-4 everywhere
+    "longmem": Workload("longmem", 99, 2, 65536, 128, 16, "f32", "f32",
+                        delta_dist="const:1e-4"),
 }
 
 
@@ -128,6 +132,11 @@ def a_matrix(dim: int, dstate: int) -> np.ndarray:
     return np.broadcast_to(-np.exp(a_log), (dim, dstate)).astype(np.float32).copy()
 
 
+def a_random(rng, dim: int, dstate: int) -> np.ndarray:
+    """A general negative A: -U(0.1, 8), different for every (d, n)."""
+    return (-rng.uniform(0.1, 8.0, size=(dim, dstate))).astype(np.float32)
+
+
 def scan_inputs(w: Workload, seed: Optional[int] = None, lti: bool = False,
                 h0: bool = False) -> dict:
     """Inputs of one ssm_scan_fwd call as float32 numpy arrays holding the
@@ -154,7 +163,7 @@ def scan_inputs(w: Workload, seed: Optional[int] = None, lti: bool = False,
         out["delta"] = _store(_delta(rng, (Bt, L, D), w.delta_dist), w.in_dtype)
         out["B"] = _store(_normal(rng, (Bt, L, N)), w.in_dtype)
         out["C"] = _store(_normal(rng, (Bt, L, N)), w.in_dtype)
-    out["A"] = a_matrix(D, N)
+    out["A"] = a_matrix(D, N) if w.a_dist == "log" else a_random(rng, D, N)
     if w.dskip_dist == "one":
         out["D"] = np.ones(D, dtype=np.float32)
     else:
