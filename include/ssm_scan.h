@@ -78,7 +78,7 @@ typedef enum {
   SSM_ERR_SHAPE = 2,       /* negative sizes, or byte counts overflow int64 */
   SSM_ERR_DTYPE = 3,       /* unknown dtype or discretization enum value */
   SSM_ERR_UNSUPPORTED = 4, /* dstate not in {1,2,4,8,16}, conv_k not in 1..4,
-                              misaligned pointer, negative chunk_len */
+                              misaligned pointer, negative chunk_len, reserved != 0 */
   SSM_ERR_ALIAS = 5,       /* an output overlaps an input or another output */
   SSM_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
   SSM_ERR_HIP = 7          /* the HIP runtime rejected a launch */
@@ -125,7 +125,8 @@ typedef struct {
   const void* Bm;                     /* (Bt, N) */
   const void* Cm;                     /* (Bt, N) */
   const float* Dskip;                 /* (D) or NULL */
-  float* h;                           /* (Bt, D, N) cached state, updated in place */
+  float* h;                           /* (Bt, D, N) cached state, updated in place;
+                                         aligned to 4 * min(N, 4) bytes */
   void* y;                            /* (Bt, D) output, read from the updated state */
 } ssm_step_args_t;
 

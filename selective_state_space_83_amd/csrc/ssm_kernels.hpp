@@ -162,18 +162,18 @@ struct ChanConst {
 };
 
 template <int N, int DISC>
-__device__ __forceinline__ void load_chan(ChanConst<N, DISC>& cc, const float* A, int64_t d,
+__device__ __forceinline__ void load_chan(ChanConst<N, DISC>& cc, const float* Arow,
                                           float thr_scale) {
-  float amax = 0.0f;
+  float amin = __builtin_inff();
 #pragma unroll
   for (int n = 0; n < N; ++n) {
-    const float a = A[d * N + n];
+    const float a = Arow[n];
     cc.A2[n] = a * kLog2e;
     if constexpr (DISC == kZoh) cc.invA[n] = (a != 0.0f) ? 1.0f / a : 0.0f;
-    amax = fmaxf(amax, (a != 0.0f) ? 1.0f / fabsf(a) : __builtin_inff());
+    amin = fminf(amin, fabsf(a));
   }
-  // min_n |Delta A[n]| < thr_scale  <=>  Delta < thr_scale * max_n 1/|A[n]|
-  cc.thr = thr_scale * amax;
+  // min_n |Delta A[n]| < thr_scale  <=>  Delta < thr_scale / min_n |A[n]|
+  cc.thr = (amin > 0.0f) ? thr_scale / amin : __builtin_inff();
 }
 
 // expm1(z) given z2 = z * log2(e) and a = exp2(z2): the series
@@ -323,7 +323,7 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
                                            float* dsum_out) {
   const int64_t d = dbase + lo;
   ChanConst<N, DISC> cc;
-  load_chan<N, DISC>(cc, p.A, d, p.exact_thr);
+  load_chan<N, DISC>(cc, p.A + d * N, p.exact_thr);
   const float dsk = (OUT && p.Dskip) ? p.Dskip[d] : 0.0f;
   ConvState cs;
   if constexpr (CONV) conv_init<InT>(cs, p, b, d, t0);
@@ -541,30 +541,89 @@ __global__ void __launch_bounds__(256) k_state_copy(float* dst, const float* src
   if (i < n) dst[i] = src ? src[i] : 0.0f;
 }
 
-// One decode step.  One lane per (b, d); b is uniform per workgroup so the B
-// and C rows are scalar loads.
+// Decode-step lane layout: a channel's N states are split over S = N / NL
+// lanes holding NL = min(N, 4) consecutive states each, so a wave covers
+// 64 / S channels and every load or store of the state h is one contiguous
+// access of the whole wave (1 KB for fp32 with N = 16).  The S partial
+// readouts of a channel are summed with quad-lane DPP swaps.
+template <int N>
+struct StepLayout {
+  static constexpr int NL = N < 4 ? N : 4;
+  static constexpr int S = N / NL;
+  static constexpr int CPW = kWave / S;   // channels per wave
+};
+
+__device__ __forceinline__ float dpp_quad_xor1(float v) {
+  // quad_perm [1, 0, 3, 2]
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float v) {
+  // quad_perm [2, 3, 0, 1]
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+// State slices of 4 / 2 / 1 floats as one vector access (the host checks that
+// h is aligned to 4 * min(N, 4) bytes).
+template <int NL>
+__device__ __forceinline__ void load_state(float (&h)[NL], const float* p) {
+  if constexpr (NL == 4) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
+  } else if constexpr (NL == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    h[0] = v.x; h[1] = v.y;
+  } else {
+    h[0] = p[0];
+  }
+}
+template <int NL>
+__device__ __forceinline__ void store_state(float* p, const float (&h)[NL]) {
+  if constexpr (NL == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(h[0], h[1], h[2], h[3]);
+  } else if constexpr (NL == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(h[0], h[1]);
+  } else {
+    p[0] = h[0];
+  }
+}
+
+// One decode step per sequence, h updated in place.  b is uniform per
+// workgroup.  Lanes past the last channel duplicate channel D - 1: they read
+// the same old state in the same load instruction and store identical values.
 template <int N, typename InT, typename OutT, int DISC>
 __global__ void __launch_bounds__(kWave) k_step(const StepParams p) {
+  constexpr int NL = StepLayout<N>::NL, S = StepLayout<N>::S, CPW = StepLayout<N>::CPW;
   const int wg = xcd_remap(blockIdx.x, p.nwg);
   const int64_t b = wg / p.dtiles;
   const int64_t dtile = wg - b * p.dtiles;
-  const int64_t d = dtile * kWave + lane_offset(dtile * kWave, p.D);
-  ChanConst<N, DISC> cc;
-  load_chan<N, DISC>(cc, p.A, d, p.exact_thr);
-  float* hp = p.h + (b * p.D + d) * N;
-  float h[N];
+  const int lane = threadIdx.x;
+  const int j = lane % S;
+  int64_t d = dtile * CPW + lane / S;
+  if (d > p.D - 1) d = p.D - 1;
+  const int n0 = j * NL;
+  ChanConst<NL, DISC> cc;
+  load_chan<NL, DISC>(cc, p.A + d * N + n0, p.exact_thr);
+  float* hp = p.h + (b * p.D + d) * N + n0;
+  float h[NL];
+  load_state<NL>(h, hp);
+  const InT* Bp = static_cast<const InT*>(p.Bm) + b * N + n0;
+  const InT* Cp = static_cast<const InT*>(p.Cm) + b * N + n0;
+  float Bv[NL], Cv[NL];
 #pragma unroll
-  for (int n = 0; n < N; ++n) h[n] = hp[n];
-  float Bv[N], Cv[N];
-  load_row<N>(Bv, static_cast<const InT*>(p.Bm) + b * N);
-  load_row<N>(Cv, static_cast<const InT*>(p.Cm) + b * N);
+  for (int n = 0; n < NL; ++n) {
+    Bv[n] = ld(Bp + n);
+    Cv[n] = ld(Cp + n);
+  }
   const float u = ld(static_cast<const InT*>(p.x) + b * p.D + d);
   const float dv = ld(static_cast<const InT*>(p.delta) + b * p.D + d);
-  const float acc = ssm_step_any<N, DISC, true>(h, cc, Bv, Cv, u, dv);
-  const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
-#pragma unroll
-  for (int n = 0; n < N; ++n) hp[n] = h[n];
-  st(static_cast<OutT*>(p.y) + b * p.D + d, fmaf(dsk, u, acc));
+  float acc = ssm_step_any<NL, DISC, true>(h, cc, Bv, Cv, u, dv);
+  if constexpr (S >= 2) acc += dpp_quad_xor1(acc);
+  if constexpr (S >= 4) acc += dpp_quad_xor2(acc);
+  store_state<NL>(hp, h);
+  if (j == 0) {
+    const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
+    st(static_cast<OutT*>(p.y) + b * p.D + d, fmaf(dsk, u, acc));
+  }
 }
 
 }  // namespace ssmk

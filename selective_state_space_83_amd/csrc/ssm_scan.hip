@@ -193,8 +193,9 @@ ssm_status_t check_step(const ssm_step_args_t* a) {
   const size_t in_sz = dtype_size(a->in_dtype), out_sz = dtype_size(a->out_dtype);
   if (misaligned(a->x, in_sz) || misaligned(a->delta, in_sz) || misaligned(a->Bm, 4) ||
       misaligned(a->Cm, 4) || misaligned(a->y, out_sz) || misaligned(a->A, 4) ||
-      misaligned(a->Dskip, 4) || misaligned(a->h, 4))
-    return fail(SSM_ERR_UNSUPPORTED, "misaligned pointer (element alignment; B, C 4 bytes)");
+      misaligned(a->Dskip, 4) || misaligned(a->h, 4 * size_t(std::min<int64_t>(a->dstate, 4))))
+    return fail(SSM_ERR_UNSUPPORTED,
+                "misaligned pointer (element alignment; B, C 4 bytes; h 4 * min(N, 4) bytes)");
   const Range y{a->y, size_t(bd) * out_sz};
   const Range h{a->h, size_t(bdn) * 4};
   const Range ins[] = {{a->x, size_t(bd) * in_sz}, {a->delta, size_t(bd) * in_sz},
@@ -205,7 +206,7 @@ ssm_status_t check_step(const ssm_step_args_t* a) {
     if (overlap(h, r)) return fail(SSM_ERR_ALIAS, "h overlaps an input");
   }
   if (overlap(y, h)) return fail(SSM_ERR_ALIAS, "y overlaps h");
-  if ((a->batch * ((a->dim + 63) / 64)) > kMaxGrid) return fail(SSM_ERR_SHAPE, "problem too large");
+  if ((a->batch * ((a->dim + 15) / 16)) > kMaxGrid) return fail(SSM_ERR_SHAPE, "problem too large");
   return SSM_OK;
 }
 
@@ -273,6 +274,9 @@ ssm_status_t dispatch_types(const ssm_scan_args_t* a, const ssmk::ScanParams& kp
 
 template <int N, typename InT, typename OutT>
 ssm_status_t run_step_t(const ssm_step_args_t* a, ssmk::StepParams kp, hipStream_t s) {
+  constexpr int cpw = ssmk::StepLayout<N>::CPW;
+  kp.dtiles = int32_t((a->dim + cpw - 1) / cpw);
+  kp.nwg = int32_t(a->batch * kp.dtiles);
   if (a->disc == SSM_DISC_ZOH)
     hipLaunchKernelGGL((ssmk::k_step<N, InT, OutT, ssmk::kZoh>), dim3(kp.nwg), dim3(ssmk::kWave), 0,
                        s, kp);
@@ -377,8 +381,6 @@ ssm_status_t ssm_step(const ssm_step_args_t* a, void* hip_stream) {
   kp.y = a->y;
   kp.Bt = a->batch;
   kp.D = a->dim;
-  kp.dtiles = int32_t((a->dim + 63) / 64);
-  kp.nwg = int32_t(a->batch * kp.dtiles);
   kp.exact_thr = exact_threshold(a->disc, a->in_dtype);
   switch (a->dstate) {
     case 1: return run_step_n<1>(a, kp, s);
