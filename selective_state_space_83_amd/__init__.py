@@ -249,6 +249,46 @@ def scan(x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None, zoh=False
     return y, h_last
 
 
+class PreparedScan:
+    """A scan whose arguments are validated and marshalled once, for callers
+    that run the same shapes and buffers repeatedly (a decode loop, a
+    benchmark, stream capture).  ``run()`` only launches; the tensors passed
+    to ``prepare_scan`` must stay alive and unchanged in place/shape."""
+
+    def __init__(self, args: ScanArgs, keep: tuple):
+        self.args = args
+        self._keep = keep          # tensors whose pointers are in args
+        self._lib = load_library()
+
+    def run(self, stream=None, events=None):
+        if events is not None:
+            self.args.ev_main_start, self.args.ev_main_stop = events
+        else:
+            self.args.ev_main_start = self.args.ev_main_stop = None
+        status = self._lib.ssm_scan_fwd(ctypes.byref(self.args), _stream_handle(stream))
+        _raise_for(self._lib, status)
+
+
+def prepare_scan(x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None, zoh=False,
+                 y=None, h_last=None, chunk_len=0, workspace=None, out_dtype=None):
+    """Allocate outputs and workspace (if not given), check and marshal the
+    arguments once; returns (PreparedScan, y, h_last)."""
+    torch = _torch()
+    lib = load_library()
+    if y is None:
+        y = torch.empty(x.shape, dtype=out_dtype if out_dtype is not None else x.dtype,
+                        device=x.device)
+    args = make_scan_args(x, delta, A, B, C, D, h0, h_last, y, conv_w, conv_b, zoh, chunk_len)
+    need = int(lib.ssm_scan_workspace_size(ctypes.byref(args)))
+    if need > 0 and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if need > 0:
+        args.workspace = _ptr(workspace)
+        args.workspace_bytes = workspace.numel()
+    keep = (x, delta, A, B, C, D, h0, h_last, y, conv_w, conv_b, workspace)
+    return PreparedScan(args, keep), y, h_last
+
+
 def make_step_args(h, x, delta, A, B, C, D=None, y=None, zoh=False) -> StepArgs:
     if h.dim() != 3 or x.dim() != 2:
         raise ValueError("h must be (batch, dim, N) and x (batch, dim)")

@@ -293,7 +293,7 @@ __device__ __forceinline__ Tile tile_of(int wg, int64_t dtiles, int64_t nchunks)
 // the time loop shared by the summary and output passes
 // ---------------------------------------------------------------------------
 
-constexpr int kUnroll = 8;   // time steps whose x / Delta loads are batched
+constexpr int kUnroll = 4;   // time steps whose x / Delta loads are batched
 
 // Vector access at a wave-uniform base plus a 32-bit per-lane byte offset:
 // lets the compiler use the SGPR-base + VGPR-offset addressing form, so no
@@ -387,14 +387,15 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
     }
   }
   for (int32_t blk = 0; blk < nblk; ++blk) {
+    // Prefetch the next block's x / Delta.  The loads are unconditional (the
+    // last block re-reads its own rows) so that the number of loads in flight
+    // is the same on every path and each wait covers only the older loads.
     float xn[kUnroll], dn[kUnroll];
-    const bool more = blk + 1 < nblk;
-    if (more) {
+    const int64_t nadv = (blk + 1 < nblk) ? int64_t(kUnroll) * D : 0;
 #pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        xn[j] = ldo(xrow + (kUnroll + j) * D, lo_in);
-        dn[j] = ldo(drow + (kUnroll + j) * D, lo_in);
-      }
+    for (int j = 0; j < kUnroll; ++j) {
+      xn[j] = ldo(xrow + nadv + j * D, lo_in);
+      dn[j] = ldo(drow + nadv + j * D, lo_in);
     }
     const int32_t tb = blk * kUnroll;
 #pragma unroll
@@ -410,10 +411,8 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
     }
     xrow += kUnroll * D;
     drow += kUnroll * D;
-    if (more) {
 #pragma unroll
-      for (int j = 0; j < kUnroll; ++j) { xc[j] = xn[j]; dc[j] = dn[j]; }
-    }
+    for (int j = 0; j < kUnroll; ++j) { xc[j] = xn[j]; dc[j] = dn[j]; }
   }
   // remainder (fewer than kUnroll steps); the current rows are in Bb0 / Cb0
   for (int32_t t = nblk * kUnroll; t < steps; ++t) {

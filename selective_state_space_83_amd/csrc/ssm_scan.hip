@@ -23,12 +23,13 @@ ssm_status_t fail(ssm_status_t s, const char* fmt, ...) {
   return s;
 }
 
-// The plan targets MI355X: 256 CUs x 4 SIMDs.  A chunked plan aims at about
-// kTargetWaves waves in the output pass (three per SIMD), and never cuts chunks
-// shorter than kMinChunk steps.
-constexpr int64_t kTargetWaves = 3072;
+// The plan targets MI355X: 256 CUs x 4 SIMDs, and scan kernels small enough
+// for four waves per SIMD.  A chunked plan uses at most kTargetWaves waves in
+// the output pass (rounding the chunk count down, so no partial extra round
+// of waves forms a tail), and never cuts chunks shorter than kMinChunk steps.
+constexpr int64_t kTargetWaves = 4096;
 constexpr int64_t kMinChunk = 64;
-constexpr int64_t kChunkAlign = 8;
+constexpr int64_t kChunkAlign = 4;
 constexpr int64_t kMaxChunk = int64_t(1) << 30;   // kernels count steps in 32 bits
 constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 
@@ -64,7 +65,7 @@ Plan make_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t chunk_len) {
     T = std::min<int64_t>(chunk_len, L);
   } else {
     const int64_t waves = Bt * pl.dtiles;
-    int64_t C = (kTargetWaves + waves - 1) / waves;
+    int64_t C = kTargetWaves / waves;
     C = std::max<int64_t>(1, std::min<int64_t>(C, L / kMinChunk));
     T = (L + C - 1) / C;
     if (C > 1) T = (T + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
