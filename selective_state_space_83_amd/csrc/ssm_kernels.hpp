@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ssmk {
 
 using bf16_t = uint16_t;
@@ -293,18 +295,45 @@ __device__ __forceinline__ Tile tile_of(int wg, int64_t dtiles, int64_t nchunks)
 // the time loop shared by the summary and output passes
 // ---------------------------------------------------------------------------
 
-constexpr int kUnroll = 4;   // time steps whose x / Delta loads are batched
+// Time steps whose x / Delta loads are batched (and prefetched one batch
+// ahead): the summary pass does less arithmetic per step, so it looks
+// further ahead to cover the same memory latency.
+constexpr int kUnrollOut = 4;
+#ifndef SSM_UNROLL_SUM
+#define SSM_UNROLL_SUM 8
+#endif
+constexpr int kUnrollSum = SSM_UNROLL_SUM;
 
-// Vector access at a wave-uniform base plus a 32-bit per-lane byte offset:
-// lets the compiler use the SGPR-base + VGPR-offset addressing form, so no
-// per-lane 64-bit address arithmetic is spent on the streams.
+// Streams through buffer resources: the wave-uniform chunk base and size sit
+// in an SGPR descriptor, the lane's byte offset is a constant VGPR and the
+// row's byte offset an SGPR advanced with scalar adds, so the vector memory
+// instructions need no per-lane address arithmetic at all.  Accesses past
+// the descriptor's size return 0 / are dropped by the hardware.
+constexpr int kBufferFlags = 0x00020000;   // gfx9-family raw buffer, 32-bit data
+
 template <typename T>
-__device__ __forceinline__ float ldo(const T* base, uint32_t byte_off) {
-  return ld(reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const T* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kBufferFlags);
 }
-template <typename T>
-__device__ __forceinline__ void sto(T* base, uint32_t byte_off, float v) {
-  st(reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off), v);
+
+__device__ __forceinline__ float ldb(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                     float*) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ float ldb(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                     bf16_t*) {
+  return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0))
+                         << 16);
+}
+__device__ __forceinline__ void stb(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                    float v, float*) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+}
+__device__ __forceinline__ void stb(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                    float v, bf16_t*) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(bf16_t, static_cast<__bf16>(v)), r,
+                                        voff, soff, 0);
 }
 
 // Lanes past the last channel (D not a multiple of 64) run channel D - 1
@@ -321,6 +350,7 @@ template <int N, typename InT, typename OutT, int DISC, bool CONV, bool OUT>
 __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64_t dbase,
                                            uint32_t lo, int64_t t0, int32_t steps, float (&h)[N],
                                            float* dsum_out) {
+  constexpr int kU = OUT ? kUnrollOut : kUnrollSum;
   const int64_t d = dbase + lo;
   ChanConst<N, DISC> cc;
   load_chan<N, DISC>(cc, p.A + d * N, p.exact_thr);
@@ -331,11 +361,22 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
   const int64_t D = p.D;
   const uint32_t lo_in = lo * sizeof(InT);
   const uint32_t lo_out = lo * sizeof(OutT);
-  const InT* xrow = static_cast<const InT*>(p.x) + (b * p.L + t0) * D + dbase;
-  const InT* drow = static_cast<const InT*>(p.delta) + (b * p.L + t0) * D + dbase;
+  // x, Delta (and y) of this wave's chunk: rows of D elements starting at
+  // (b, t0, dbase); the plan keeps steps * D * 4 bytes below 2^31
+  const int64_t chunk_base = (b * p.L + t0) * D + dbase;
+  const uint32_t row_in = static_cast<uint32_t>(D * sizeof(InT));
+  const uint32_t span_in = static_cast<uint32_t>(steps) * row_in;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const InT*>(p.x) + chunk_base, span_in);
+  const __amdgpu_buffer_rsrc_t rd =
+      make_rsrc(static_cast<const InT*>(p.delta) + chunk_base, span_in);
+  const uint32_t row_out = static_cast<uint32_t>(D * sizeof(OutT));
+  // (the summary pass writes no y: its descriptor then covers nothing)
+  const __amdgpu_buffer_rsrc_t ry =
+      make_rsrc(static_cast<OutT*>(p.y) + (OUT ? chunk_base : 0),
+                OUT ? static_cast<uint32_t>(steps) * row_out : 0u);
+  uint32_t soff_in = 0, soff_out = 0;
   const InT* Brow = static_cast<const InT*>(p.Bm) + (b * p.L + t0) * N;
   const InT* Crow = static_cast<const InT*>(p.Cm) + (b * p.L + t0) * N;
-  OutT* yrow = OUT ? static_cast<OutT*>(p.y) + (b * p.L + t0) * D + dbase : nullptr;
 
   float dacc = 0.0f;
   if (steps <= 0) return;
@@ -350,13 +391,27 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
                       float (&Ccur)[N], float (&Cnext)[N]) {
     // on the last step re-read the current row instead of running past the end
     const int64_t adv = has_next ? N : 0;
-    load_row<N>(Bnext, Brow + adv);
-    if constexpr (OUT) load_row<N>(Cnext, Crow + adv);
+    const InT* nb = Brow + adv;
+    const InT* nc = Crow + adv;
+    // Scalar loads complete out of order, so the only wait for them is "all
+    // outstanding".  The next step's rows must therefore be requested after
+    // this step's rows have been waited for, or every use of the current row
+    // would also wait for the prefetch.  Reading the current rows here (no
+    // code is emitted) puts that wait before the two loads below.
+    // (Single-state rows may live in VGPRs; they are not worth ordering.)
+    constexpr bool kScalarRows = N >= 2;
+    if constexpr (kScalarRows && OUT) {
+      asm volatile("" : "+s"(nb), "+s"(nc) : "s"(Bcur[0]), "s"(Ccur[0]));
+    } else if constexpr (kScalarRows) {
+      asm volatile("" : "+s"(nb) : "s"(Bcur[0]));
+    }
+    load_row<N>(Bnext, nb);
+    if constexpr (OUT) load_row<N>(Cnext, nc);
     const float u = CONV ? conv_push(cs, xv) : xv;
     if constexpr (OUT) {
       const float acc = ssm_step_any<N, DISC, true>(h, cc, Bcur, Ccur, u, dv);
-      sto(yrow, lo_out, fmaf(dsk, u, acc));
-      yrow += D;
+      stb(ry, lo_out, soff_out, fmaf(dsk, u, acc), static_cast<OutT*>(nullptr));
+      soff_out += row_out;
     } else {
       ssm_step_any<N, DISC, false>(h, cc, Bcur, Bcur, u, dv);
     }
@@ -365,7 +420,7 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
   };
 
   // The chunk's sum of Delta feeds exp(A * sum) in the carry combine, so it
-  // is kept accurate: block sums of kUnroll steps are added with Kahan
+  // is kept accurate: block sums of kU steps are added with Kahan
   // compensation (a plain running fp32 sum of a steady Delta drifts by
   // ~length * 2^-25 relative, which the decay amplifies by |A * sum|).
   float dcomp = 0.0f;
@@ -376,48 +431,48 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
     dacc = tv;
   };
 
-  static_assert(kUnroll % 2 == 0, "row buffers alternate within a block");
-  const int32_t nblk = steps / kUnroll;
-  float xc[kUnroll], dc[kUnroll];
+  static_assert(kU % 2 == 0, "row buffers alternate within a block");
+  const int32_t nblk = steps / kU;
+  float xc[kU], dc[kU];
+  constexpr InT* kIn = nullptr;
   if (nblk > 0) {
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      xc[j] = ldo(xrow + j * D, lo_in);
-      dc[j] = ldo(drow + j * D, lo_in);
+    for (int j = 0; j < kU; ++j) {
+      xc[j] = ldb(rx, lo_in, j * row_in, kIn);
+      dc[j] = ldb(rd, lo_in, j * row_in, kIn);
     }
   }
   for (int32_t blk = 0; blk < nblk; ++blk) {
     // Prefetch the next block's x / Delta.  The loads are unconditional (the
     // last block re-reads its own rows) so that the number of loads in flight
     // is the same on every path and each wait covers only the older loads.
-    float xn[kUnroll], dn[kUnroll];
-    const int64_t nadv = (blk + 1 < nblk) ? int64_t(kUnroll) * D : 0;
+    float xn[kU], dn[kU];
+    const uint32_t nsoff = soff_in + ((blk + 1 < nblk) ? kU * row_in : 0u);
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      xn[j] = ldo(xrow + nadv + j * D, lo_in);
-      dn[j] = ldo(drow + nadv + j * D, lo_in);
+    for (int j = 0; j < kU; ++j) {
+      xn[j] = ldb(rx, lo_in, nsoff + j * row_in, kIn);
+      dn[j] = ldb(rd, lo_in, nsoff + j * row_in, kIn);
     }
-    const int32_t tb = blk * kUnroll;
+    const int32_t tb = blk * kU;
 #pragma unroll
-    for (int j = 0; j < kUnroll; j += 2) {
+    for (int j = 0; j < kU; j += 2) {
       one_step(xc[j], dc[j], tb + j + 1 < steps, Bb0, Bb1, Cb0, Cb1);
       one_step(xc[j + 1], dc[j + 1], tb + j + 2 < steps, Bb1, Bb0, Cb1, Cb0);
     }
     if constexpr (!OUT) {
       float bs = dc[0];
 #pragma unroll
-      for (int j = 1; j < kUnroll; ++j) bs += dc[j];
+      for (int j = 1; j < kU; ++j) bs += dc[j];
       sum_add(bs);
     }
-    xrow += kUnroll * D;
-    drow += kUnroll * D;
+    soff_in += kU * row_in;
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) { xc[j] = xn[j]; dc[j] = dn[j]; }
+    for (int j = 0; j < kU; ++j) { xc[j] = xn[j]; dc[j] = dn[j]; }
   }
-  // remainder (fewer than kUnroll steps); the current rows are in Bb0 / Cb0
-  for (int32_t t = nblk * kUnroll; t < steps; ++t) {
-    const float xv = ldo(xrow, lo_in);
-    const float dv = ldo(drow, lo_in);
+  // remainder (fewer than kU steps); the current rows are in Bb0 / Cb0
+  for (int32_t t = nblk * kU; t < steps; ++t) {
+    const float xv = ldb(rx, lo_in, soff_in, kIn);
+    const float dv = ldb(rd, lo_in, soff_in, kIn);
     one_step(xv, dv, t + 1 < steps, Bb0, Bb1, Cb0, Cb1);
     if constexpr (!OUT) sum_add(dv);
 #pragma unroll
@@ -425,8 +480,7 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
       Bb0[n] = Bb1[n];
       if constexpr (OUT) Cb0[n] = Cb1[n];
     }
-    xrow += D;
-    drow += D;
+    soff_in += row_in;
   }
   if (!OUT && dsum_out) *dsum_out = dacc - dcomp;
 }

@@ -31,6 +31,9 @@ constexpr int64_t kTargetWaves = 4096;
 constexpr int64_t kMinChunk = 64;
 constexpr int64_t kChunkAlign = 4;
 constexpr int64_t kMaxChunk = int64_t(1) << 30;   // kernels count steps in 32 bits
+// A chunk's rows of x / Delta / y are addressed through one buffer resource
+// with 32-bit offsets: keep steps * D * 4 bytes below 2^31.
+constexpr int64_t kMaxChunkBytes = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 
 size_t dtype_size(int32_t dt) { return dt == SSM_BF16 ? 2 : 4; }
@@ -71,7 +74,7 @@ Plan make_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t chunk_len) {
     if (C > 1) T = (T + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
     T = std::min(T, L);
   }
-  pl.T = std::min(T, kMaxChunk);
+  pl.T = std::min({T, kMaxChunk, std::max<int64_t>(1, kMaxChunkBytes / (D * 4))});
   pl.C = (L + pl.T - 1) / pl.T;
   if (pl.C > 1) {
     pl.ws_dsum = align256(size_t(Bt) * size_t(pl.C - 1) * size_t(D) * 4);
