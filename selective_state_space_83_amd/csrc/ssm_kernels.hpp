@@ -604,6 +604,7 @@ struct StepLayout {
   static constexpr int NL = N < 4 ? N : 4;
   static constexpr int S = N / NL;
   static constexpr int CPW = kWave / S;   // channels per wave
+  static constexpr int ROWS = 2;          // batch rows per wave (more state in flight)
 };
 
 __device__ __forceinline__ float dpp_quad_xor1(float v) {
@@ -640,15 +641,18 @@ __device__ __forceinline__ void store_state(float* p, const float (&h)[NL]) {
   }
 }
 
-// One decode step per sequence, h updated in place.  b is uniform per
-// workgroup.  Lanes past the last channel duplicate channel D - 1: they read
-// the same old state in the same load instruction and store identical values.
+// One decode step per sequence, h updated in place.  A wave covers CPW
+// channels of ROWS consecutive batch rows (a row past the batch is skipped,
+// uniformly for the wave).  Lanes past the last channel duplicate channel
+// D - 1: they read the same old state in the same load instruction and store
+// identical values.
 template <int N, typename InT, typename OutT, int DISC>
 __global__ void __launch_bounds__(kWave) k_step(const StepParams p) {
   constexpr int NL = StepLayout<N>::NL, S = StepLayout<N>::S, CPW = StepLayout<N>::CPW;
+  constexpr int ROWS = StepLayout<N>::ROWS;
   const int wg = xcd_remap(blockIdx.x, p.nwg);
-  const int64_t b = wg / p.dtiles;
-  const int64_t dtile = wg - b * p.dtiles;
+  const int64_t bt = wg / p.dtiles;
+  const int64_t dtile = wg - bt * p.dtiles;
   const int lane = threadIdx.x;
   const int j = lane % S;
   int64_t d = dtile * CPW + lane / S;
@@ -656,26 +660,29 @@ __global__ void __launch_bounds__(kWave) k_step(const StepParams p) {
   const int n0 = j * NL;
   ChanConst<NL, DISC> cc;
   load_chan<NL, DISC>(cc, p.A + d * N + n0, p.exact_thr);
-  float* hp = p.h + (b * p.D + d) * N + n0;
-  float h[NL];
-  load_state<NL>(h, hp);
-  const InT* Bp = static_cast<const InT*>(p.Bm) + b * N + n0;
-  const InT* Cp = static_cast<const InT*>(p.Cm) + b * N + n0;
-  float Bv[NL], Cv[NL];
+  const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
 #pragma unroll
-  for (int n = 0; n < NL; ++n) {
-    Bv[n] = ld(Bp + n);
-    Cv[n] = ld(Cp + n);
-  }
-  const float u = ld(static_cast<const InT*>(p.x) + b * p.D + d);
-  const float dv = ld(static_cast<const InT*>(p.delta) + b * p.D + d);
-  float acc = ssm_step_any<NL, DISC, true>(h, cc, Bv, Cv, u, dv);
-  if constexpr (S >= 2) acc += dpp_quad_xor1(acc);
-  if constexpr (S >= 4) acc += dpp_quad_xor2(acc);
-  store_state<NL>(hp, h);
-  if (j == 0) {
-    const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
-    st(static_cast<OutT*>(p.y) + b * p.D + d, fmaf(dsk, u, acc));
+  for (int r = 0; r < ROWS; ++r) {
+    const int64_t b = bt * ROWS + r;
+    if (b >= p.Bt) break;
+    float* hp = p.h + (b * p.D + d) * N + n0;
+    float h[NL];
+    load_state<NL>(h, hp);
+    const InT* Bp = static_cast<const InT*>(p.Bm) + b * N + n0;
+    const InT* Cp = static_cast<const InT*>(p.Cm) + b * N + n0;
+    float Bv[NL], Cv[NL];
+#pragma unroll
+    for (int n = 0; n < NL; ++n) {
+      Bv[n] = ld(Bp + n);
+      Cv[n] = ld(Cp + n);
+    }
+    const float u = ld(static_cast<const InT*>(p.x) + b * p.D + d);
+    const float dv = ld(static_cast<const InT*>(p.delta) + b * p.D + d);
+    float acc = ssm_step_any<NL, DISC, true>(h, cc, Bv, Cv, u, dv);
+    if constexpr (S >= 2) acc += dpp_quad_xor1(acc);
+    if constexpr (S >= 4) acc += dpp_quad_xor2(acc);
+    store_state<NL>(hp, h);
+    if (j == 0) st(static_cast<OutT*>(p.y) + b * p.D + d, fmaf(dsk, u, acc));
   }
 }
 

@@ -259,6 +259,42 @@ def test_decode_equals_scan():
         G.compare(h.cpu().numpy(), h_scan, tol, "decode vs scan h")
 
 
+# (batch, D, N, in, out, zoh, skip)
+STEP_SMALL = [
+    (1, 1, 1, "f32", "f32", False, True),
+    (3, 65, 2, "f32", "bf16", True, False),
+    (5, 130, 4, "bf16", "bf16", False, True),
+    (2, 63, 8, "f32", "f32", True, True),
+    (7, 129, 16, "bf16", "f32", True, True),
+    (4, 2, 16, "f32", "f32", False, False),
+    (9, 200, 1, "bf16", "bf16", True, True),
+]
+
+
+@pytest.mark.parametrize("case", STEP_SMALL, ids=lambda c: "b%d_D%d_N%d_%s_%s_zoh%d_skip%d" % c)
+def test_step_small_shapes(case):
+    """Eight consecutive decode steps on a state updated in place, every
+    element of y and h compared with the oracle's decode step."""
+    Bt, D, N, idt, odt, zoh, skip = case
+    w = SI.Workload("s", 40 + STEP_SMALL.index(case), Bt, 8, D, N, idt, odt, zoh=zoh,
+                    a_dist="random", dskip_dist="uniform")
+    inp = SI.scan_inputs(w, seed=5, h0=True)
+    h = G.dev(inp["h0"])
+    A = G.dev(inp["A"])
+    Dv = G.dev(inp["D"]) if skip else None
+    hr = inp["h0"].astype(np.float64)
+    orc = oracle.default()
+    tol = G.y_tol(idt, odt)
+    for t in range(8):
+        yt = ssm.step(h, G.dev(inp["x"][:, t], idt), G.dev(inp["delta"][:, t], idt), A,
+                      G.dev(inp["B"][:, t], idt), G.dev(inp["C"][:, t], idt), Dv, zoh=zoh,
+                      out_dtype=G.torch_dtype(odt))
+        yr, hr = orc.step(hr, inp["x"][:, t], inp["delta"][:, t], inp["A"], inp["B"][:, t],
+                          inp["C"][:, t], inp["D"] if skip else None, zoh=zoh)
+        G.compare(G.host(yt), yr, tol, "step %d y" % t)
+        G.compare(h.cpu().numpy(), hr, G.TOL[idt], "step %d h" % t)
+
+
 def test_bitwise_deterministic():
     inp = _medium_inputs(L=5000, D=300, conv=4)
     runs = [G.gpu_scan(inp, "f32", "f32", h0=True) for _ in range(3)]
