@@ -40,11 +40,12 @@ class Oracle:
         lib = ctypes.CDLL(path)
         dp = ctypes.POINTER(ctypes.c_double)
         i64 = ctypes.c_int64
-        lib.ssm_ref_scan_f64.argtypes = [i64, i64, i64, i64, dp, dp, dp, dp, dp, dp, dp,
-                                         dp, dp, i64, ctypes.c_int, dp, dp, ctypes.c_int]
+        ci = ctypes.c_int
+        lib.ssm_ref_scan_f64.argtypes = [i64, i64, i64, i64, dp, dp, dp, ci, dp, dp, dp, dp,
+                                         dp, dp, dp, dp, i64, dp, ci, dp, dp, dp, ci]
         lib.ssm_ref_scan_f64.restype = ctypes.c_int
-        lib.ssm_ref_step_f64.argtypes = [i64, i64, i64, dp, dp, dp, dp, dp, dp, dp,
-                                         ctypes.c_int, dp, ctypes.c_int]
+        lib.ssm_ref_step_f64.argtypes = [i64, i64, i64, dp, dp, dp, dp, ci, dp, dp, dp, dp,
+                                         dp, dp, dp, i64, dp, ci, dp, ci]
         lib.ssm_ref_step_f64.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -62,54 +63,80 @@ class Oracle:
         return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
     def scan(self, x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None,
-             zoh=False, want_h_last=True, nthreads=0):
-        """Return (y, h_last) in float64.  Shapes: x, delta (batch, L, dim);
-        A (dim, N); B, C (batch, L, N); D (dim,); h0 (batch, dim, N);
-        conv_w (dim, K); conv_b (dim,)."""
+             zoh=False, want_h_last=True, nthreads=0, delta_bias=None, delta_softplus=False,
+             z=None, conv_state_in=None, conv_state_out=None):
+        """Return (y, h_last) in float64.  Shapes: x, delta, z (batch, L, dim);
+        A (dim, N); B, C (batch, L, N); D, delta_bias (dim,); h0 (batch, dim,
+        N); conv_w (dim, K); conv_b (dim,); conv_state_in (batch, dim, K-1).
+        ``conv_state_out``, a float64 array of shape (batch, dim, K-1), is
+        filled with the last K-1 inputs when given."""
         x, delta, A, B, C = map(self._f64, (x, delta, A, B, C))
         D, h0, conv_w, conv_b = map(self._f64, (D, h0, conv_w, conv_b))
+        delta_bias, z, conv_state_in = map(self._f64, (delta_bias, z, conv_state_in))
         batch, L, dim = x.shape
         N = A.shape[1]
         assert delta.shape == x.shape and A.shape == (dim, N)
         assert B.shape == (batch, L, N) and C.shape == (batch, L, N)
-        if D is not None:
-            assert D.shape == (dim,)
-        if h0 is not None:
-            assert h0.shape == (batch, dim, N)
+        for v, shp in ((D, (dim,)), (delta_bias, (dim,)), (h0, (batch, dim, N)),
+                       (z, x.shape)):
+            if v is not None:
+                assert v.shape == shp, (v.shape, shp)
         K = 0
         if conv_w is not None:
             assert conv_w.ndim == 2 and conv_w.shape[0] == dim
             K = conv_w.shape[1]
             if conv_b is not None:
                 assert conv_b.shape == (dim,)
+        for v in (conv_state_in, conv_state_out):
+            if v is not None:
+                assert conv_w is not None and v.shape == (batch, dim, K - 1)
+        if conv_state_out is not None:
+            assert conv_state_out.dtype == np.float64 and conv_state_out.flags.c_contiguous
         y = np.zeros((batch, L, dim), dtype=np.float64)
         h_last = np.zeros((batch, dim, N), dtype=np.float64) if want_h_last else None
         rc = self.lib.ssm_ref_scan_f64(batch, L, dim, N, self._ptr(x), self._ptr(delta),
+                                       self._ptr(delta_bias), int(bool(delta_softplus)),
                                        self._ptr(A), self._ptr(B), self._ptr(C), self._ptr(D),
-                                       self._ptr(h0), self._ptr(conv_w), self._ptr(conv_b), K,
+                                       self._ptr(z), self._ptr(h0), self._ptr(conv_w),
+                                       self._ptr(conv_b), K, self._ptr(conv_state_in),
                                        int(bool(zoh)), self._ptr(y), self._ptr(h_last),
-                                       int(nthreads))
+                                       self._ptr(conv_state_out), int(nthreads))
         if rc != 0:
             raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
         return y, h_last
 
-    def step(self, h, x, delta, A, B, C, D=None, zoh=False, nthreads=0):
-        """One decode step.  Returns (y, h_new) in float64; ``h`` is not
-        modified.  Shapes: h (batch, dim, N); x, delta (batch, dim);
-        B, C (batch, N)."""
+    def step(self, h, x, delta, A, B, C, D=None, zoh=False, nthreads=0, delta_bias=None,
+             delta_softplus=False, z=None, conv_w=None, conv_b=None, conv_state=None):
+        """One decode step.  Returns (y, h_new) in float64, or (y, h_new,
+        conv_state_new) when ``conv_w`` is given; the inputs are not modified.
+        Shapes: h (batch, dim, N); x, delta, z (batch, dim); B, C (batch, N);
+        conv_w (dim, K); conv_state (batch, dim, K-1)."""
         h = np.array(h, dtype=np.float64, copy=True, order="C")
         x, delta, A, B, C, D = map(self._f64, (x, delta, A, B, C, D))
+        delta_bias, z, conv_w, conv_b = map(self._f64, (delta_bias, z, conv_w, conv_b))
         batch, dim, N = h.shape
         assert x.shape == (batch, dim) and delta.shape == (batch, dim)
         assert A.shape == (dim, N) and B.shape == (batch, N) and C.shape == (batch, N)
+        if z is not None:
+            assert z.shape == (batch, dim)
+        K = 0
+        cs = None
+        if conv_w is not None:
+            K = conv_w.shape[1]
+            assert conv_w.shape == (dim, K)
+            cs = (np.zeros((batch, dim, K - 1)) if conv_state is None else
+                  np.array(conv_state, dtype=np.float64, copy=True, order="C"))
+            assert cs.shape == (batch, dim, K - 1)
         y = np.zeros((batch, dim), dtype=np.float64)
         rc = self.lib.ssm_ref_step_f64(batch, dim, N, self._ptr(h), self._ptr(x),
-                                       self._ptr(delta), self._ptr(A), self._ptr(B),
-                                       self._ptr(C), self._ptr(D), int(bool(zoh)),
-                                       self._ptr(y), int(nthreads))
+                                       self._ptr(delta), self._ptr(delta_bias),
+                                       int(bool(delta_softplus)), self._ptr(A), self._ptr(B),
+                                       self._ptr(C), self._ptr(D), self._ptr(z),
+                                       self._ptr(conv_w), self._ptr(conv_b), K, self._ptr(cs),
+                                       int(bool(zoh)), self._ptr(y), int(nthreads))
         if rc != 0:
             raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
-        return y, h
+        return (y, h) if conv_w is None else (y, h, cs)
 
 
 _default = None

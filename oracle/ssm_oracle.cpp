@@ -30,7 +30,22 @@
 //     returns the scan plus self.D * x_conv);
 //   * the causal depthwise conv1d prologue, PyTorch Conv1d semantics with
 //     padding K-1 keeping the first L outputs, followed by SiLU
-//     silu(z) = z / (1 + exp(-z)) (gsyq.cn SelectiveSSM.__init__ / forward).
+//     silu(z) = z / (1 + exp(-z)) (gsyq.cn SelectiveSSM.__init__ / forward);
+//   * optionally the step size is produced here from its pre-activation:
+//     Delta = softplus(delta + bias[d]), softplus(v) = log(1 + exp(v)), the
+//     bias being the per-channel bias of the Delta projection (gsyq.cn,
+//     section "选择性的数学解析", Delta = Softplus(Linear(x)); VMamba note,
+//     section "mamba：从S4到S6的算法变化流程", tau_Delta = softplus);
+//   * optionally the output is gated by a second input stream z of the same
+//     shape as x: out = y * silu(z) (the gated-MLP branch the Mamba block
+//     adds around the SSM: VMamba note, section "简化的SSM架构"; the page's
+//     figure with the formula is lost, so this is a reading);
+//   * optionally the conv window continues across calls: conv_state_in holds
+//     the K-1 inputs before token 0 (oldest first; zeros when absent) and
+//     conv_state_out receives the last K-1 inputs, so a sequence scanned in
+//     two calls, or a prefill followed by decode steps, sees the same window
+//     as one call (the recurrent, constant-cost-per-token inference mode:
+//     53ai.com explainer, section "一、Motivation").
 //
 // Readings where the pages are silent (listed in the design notes too):
 //   - the initial state h0 precedes token 0, so y_0 already contains x_0;
@@ -50,14 +65,37 @@ namespace {
 
 struct ScanProblem {
   int64_t batch, seqlen, dim, dstate;
-  const double *x, *delta, *A, *Bm, *Cm, *Dskip, *h0;
+  const double *x, *delta, *delta_bias;
+  int delta_softplus;
+  const double *A, *Bm, *Cm, *Dskip, *z, *h0;
   const double *conv_w, *conv_b;
   int64_t conv_k;
+  const double* conv_state_in;
   int zoh;
-  double *y, *h_last;
+  double *y, *h_last, *conv_state_out;
 };
 
 double silu(double z) { return z / (1.0 + std::exp(-z)); }
+
+// softplus(v) = log(1 + exp(v)), written so that neither branch overflows.
+double softplus(double v) { return (v > 0.0 ? v : 0.0) + std::log1p(std::exp(-std::fabs(v))); }
+
+// The step size Delta[b, t, d]: the given value, plus the channel's bias when
+// one is given, through softplus when asked.
+double step_size(const ScanProblem& p, int64_t b, int64_t t, int64_t d) {
+  double v = p.delta[(b * p.seqlen + t) * p.dim + d];
+  if (p.delta_bias) v += p.delta_bias[d];
+  return p.delta_softplus ? softplus(v) : v;
+}
+
+// x[b, t, d] for -(K-1) <= t < L: before token 0 the conv window holds
+// conv_state_in[b, d, (K-1) + t] (zeros when no state is given).
+double x_at(const ScanProblem& p, int64_t b, int64_t t, int64_t d) {
+  if (t >= 0) return p.x[(b * p.seqlen + t) * p.dim + d];
+  const int64_t S = p.conv_k - 1;
+  if (!p.conv_state_in || t < -S) return 0.0;
+  return p.conv_state_in[(b * p.dim + d) * S + S + t];
+}
 
 // Input factor multiplying B[n] * u: Delta (simplified) or the ZOH factor
 // (exp(Delta A) - 1) / A, whose A -> 0 limit is Delta.
@@ -68,7 +106,7 @@ double input_factor(double dt, double a_cont, int zoh) {
 }
 
 // Scan input u[b, t, d]: x itself, or silu(bias + sum_k w[d,k] x[b, t-K+1+k, d])
-// with x taken as zero before the start of the sequence.
+// with x before the start of the sequence taken from the conv state.
 double scan_input(const ScanProblem& p, int64_t b, int64_t t, int64_t d) {
   const int64_t L = p.seqlen, D = p.dim;
   if (!p.conv_w) return p.x[(b * L + t) * D + d];
@@ -76,8 +114,7 @@ double scan_input(const ScanProblem& p, int64_t b, int64_t t, int64_t d) {
   double z = p.conv_b ? p.conv_b[d] : 0.0;
   for (int64_t k = 0; k < K; ++k) {
     const int64_t src = t - (K - 1) + k;
-    if (src < 0) continue;
-    z += p.conv_w[d * K + k] * p.x[(b * L + src) * D + d];
+    z += p.conv_w[d * K + k] * x_at(p, b, src, d);
   }
   return silu(z);
 }
@@ -89,7 +126,7 @@ void scan_channel(const ScanProblem& p, int64_t b, int64_t d, std::vector<double
   const double dskip = p.Dskip ? p.Dskip[d] : 0.0;
   for (int64_t t = 0; t < L; ++t) {
     const double u = scan_input(p, b, t, d);
-    const double dt = p.delta[(b * L + t) * D + d];
+    const double dt = step_size(p, b, t, d);
     const double* Bt = p.Bm + (b * L + t) * N;
     const double* Ct = p.Cm + (b * L + t) * N;
     double acc = 0.0;
@@ -100,10 +137,19 @@ void scan_channel(const ScanProblem& p, int64_t b, int64_t d, std::vector<double
       h[n] = abar * h[n] + bbar * u;
       acc += Ct[n] * h[n];
     }
-    p.y[(b * L + t) * D + d] = acc + dskip * u;
+    double out = acc + dskip * u;
+    if (p.z) out *= silu(p.z[(b * L + t) * D + d]);
+    p.y[(b * L + t) * D + d] = out;
   }
   if (p.h_last)
     for (int64_t n = 0; n < N; ++n) p.h_last[(b * D + d) * N + n] = h[n];
+  // the last K-1 inputs, oldest first (entry j reads conv_state_in only at
+  // index j or above, so in ascending j the state may be updated in place)
+  if (p.conv_w && p.conv_state_out) {
+    const int64_t S = p.conv_k - 1;
+    for (int64_t j = 0; j < S; ++j)
+      p.conv_state_out[(b * D + d) * S + j] = x_at(p, b, L - S + j, d);
+  }
 }
 
 void run_channels(const ScanProblem& p, int64_t first, int64_t last) {
@@ -123,22 +169,27 @@ int pick_threads(int requested, int64_t work_items) {
 extern "C" {
 
 // O1: y (batch, L, D) and optionally h_last (batch, D, N) from x, delta
-// (batch, L, D), A (D, N), B, C (batch, L, N), Dskip (D) or NULL, h0
-// (batch, D, N) or NULL, conv_w (D, K) / conv_b (D) or NULL.  All arrays are
+// (batch, L, D), delta_bias (D) or NULL, A (D, N), B, C (batch, L, N), Dskip
+// (D) or NULL, z (batch, L, D) or NULL, h0 (batch, D, N) or NULL, conv_w
+// (D, K) / conv_b (D) or NULL, conv_state_in (batch, D, K-1) or NULL; writes
+// conv_state_out (batch, D, K-1) when given with conv_w.  All arrays are
 // row-major doubles.  Returns 0, or -1 on a bad argument.  Uses `nthreads`
 // std::threads over the (b, d) channels (0 = all hardware threads).
 int ssm_ref_scan_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                     const double* x, const double* delta, const double* A,
-                     const double* Bm, const double* Cm, const double* Dskip,
+                     const double* x, const double* delta, const double* delta_bias,
+                     int delta_softplus, const double* A, const double* Bm,
+                     const double* Cm, const double* Dskip, const double* z,
                      const double* h0, const double* conv_w, const double* conv_b,
-                     int64_t conv_k, int zoh, double* y, double* h_last, int nthreads) {
+                     int64_t conv_k, const double* conv_state_in, int zoh, double* y,
+                     double* h_last, double* conv_state_out, int nthreads) {
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1) return -1;
   if (conv_w && conv_k < 1) return -1;
   if (batch * dim == 0) return 0;
   if (seqlen > 0 && (!x || !delta || !Bm || !Cm || !y)) return -1;
   if (!A) return -1;
-  ScanProblem p{batch, seqlen, dim, dstate, x, delta, A, Bm, Cm, Dskip, h0,
-                conv_w, conv_b, conv_k, zoh, y, h_last};
+  ScanProblem p{batch, seqlen, dim, dstate, x, delta, delta_bias, delta_softplus, A, Bm,
+                Cm, Dskip, z, h0, conv_w, conv_b, conv_k, conv_state_in, zoh, y, h_last,
+                conv_state_out};
   const int64_t channels = batch * dim;
   const int nt = pick_threads(nthreads, channels);
   if (nt == 1) {
@@ -155,19 +206,25 @@ int ssm_ref_scan_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
 }
 
 // O2: one decode step.  h (batch, D, N) is read and overwritten with the new
-// state; y (batch, D) = C . h_new + Dskip * x.  x, delta are (batch, D); B, C
-// are (batch, N).  Same recurrence as O1 with L = 1 and no conv prologue.
+// state; y (batch, D) = C . h_new + Dskip * u (times silu(z) when z is given).
+// x, delta, z are (batch, D); B, C are (batch, N).  With conv_w the scan input
+// u is the conv over the window conv_state (batch, D, K-1) followed by x, and
+// conv_state is shifted in place to end with x.  This is O1 with L = 1.
 int ssm_ref_step_f64(int64_t batch, int64_t dim, int64_t dstate, double* h,
-                     const double* x, const double* delta, const double* A,
-                     const double* Bm, const double* Cm, const double* Dskip,
-                     int zoh, double* y, int nthreads) {
+                     const double* x, const double* delta, const double* delta_bias,
+                     int delta_softplus, const double* A, const double* Bm,
+                     const double* Cm, const double* Dskip, const double* z,
+                     const double* conv_w, const double* conv_b, int64_t conv_k,
+                     double* conv_state, int zoh, double* y, int nthreads) {
   if (batch < 0 || dim < 0 || dstate < 1) return -1;
+  if (conv_w && (conv_k < 1 || (conv_k > 1 && !conv_state))) return -1;
   if (batch * dim == 0) return 0;
   if (!h || !x || !delta || !A || !Bm || !Cm || !y) return -1;
-  // h is both the initial and the final state; the scan reads h0[n] for a
-  // channel before it writes h_last[n] of that channel, so in-place is safe.
-  return ssm_ref_scan_f64(batch, 1, dim, dstate, x, delta, A, Bm, Cm, Dskip, h,
-                          nullptr, nullptr, 0, zoh, y, h, nthreads);
+  // h and conv_state are both input and output; the scan reads a channel's
+  // inputs before it writes that channel's outputs, so in-place is safe.
+  return ssm_ref_scan_f64(batch, 1, dim, dstate, x, delta, delta_bias, delta_softplus, A, Bm,
+                          Cm, Dskip, z, h, conv_w, conv_b, conv_k, conv_state, zoh, y, h,
+                          conv_state, nthreads);
 }
 
 }  // extern "C"

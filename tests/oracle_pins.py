@@ -14,6 +14,9 @@ Page citations (the pages are web articles on Mamba; section names as printed):
       "卷积结构表示以并行训练", "mamba：从S4到S6的算法变化流程"
   p5  joto.ai "Mamba：2 状态空间模型", sections on time invariance and
       "离散到连续" (zero-order hold)
+  p2 also: "选择性的数学解析" (Delta = Softplus(Linear(x)));
+  p3 also: "简化的SSM架构" (the gated block around the SSM)
+  p1 also: "一、Motivation" (recurrent inference with a carried state)
 """
 from __future__ import annotations
 
@@ -463,10 +466,192 @@ def pin_conv_scan_brute(orc):
         _rel_close(y, ref, 1e-12, "conv+scan zoh=%s" % zoh)
 
 
+# --------------------------------------------------------------------------
+# P10: step size from its pre-activation, Delta = softplus(v + bias[d])
+#      (p2 "选择性的数学解析": Delta = Softplus(Linear(x)); p3 "mamba：从S4到S6
+#      的算法变化流程": tau_Delta = softplus)
+# --------------------------------------------------------------------------
+
+def pin_softplus_delta(orc):
+    """The fused form equals the scan fed with numpy's log(exp(0) + exp(v))
+    of the biased pre-activation, for both discretizations, with the conv
+    prologue and with pre-activations far into both tails."""
+    rng = _rng(110)
+    Bt, L, D, N, K = 2, 30, 4, 3, 4
+    x, _, A, B, C, Dsk = _random_problem(rng, Bt, L, D, N)
+    raw = rng.normal(-2.0, 3.0, (Bt, L, D))
+    raw[0, :4, 0] = [-60.0, -35.0, 35.0, 60.0]
+    bias = rng.normal(0.0, 1.0, D)
+    w = rng.standard_normal((D, K))
+    cb = rng.standard_normal(D)
+    for zoh in (False, True):
+        for conv in (False, True):
+            kw = dict(D=Dsk, zoh=zoh, conv_w=w if conv else None, conv_b=cb if conv else None)
+            y, h = orc.scan(x, raw, A, B, C, delta_bias=bias, delta_softplus=True, **kw)
+            y_ref, h_ref = orc.scan(x, np.logaddexp(0.0, raw + bias), A, B, C, **kw)
+            _rel_close(y, y_ref, 1e-13, "softplus y zoh=%s conv=%s" % (zoh, conv))
+            _rel_close(h, h_ref, 1e-13, "softplus h zoh=%s conv=%s" % (zoh, conv))
+    # a bias without softplus is a plain shift
+    y, _ = orc.scan(x, raw + 5.0, A, B, C, D=Dsk, delta_bias=bias)
+    y_ref, _ = orc.scan(x, raw + 5.0 + bias, A, B, C, D=Dsk)
+    _rel_close(y, y_ref, 1e-13, "bias only")
+
+
+def pin_softplus_values(orc):
+    """With one state, h0 = 0, A = -1, B = C = x = 1 and no skip, a single
+    Delta*B step outputs Delta itself.  Closed forms: softplus(0) = ln 2,
+    softplus(ln(e - 1)) = 1, softplus(v) = v + log1p(exp(-v)) and
+    softplus(-v) = log1p(exp(-v)); each checked to 1e-14 relative, the tiny
+    ones included (log(1 + exp(v)) evaluated naively loses them entirely)."""
+    v = np.array([0.0, math.log(math.e - 1.0), 40.0, -40.0, -700.0, 2.5])
+    ref = np.array([math.log(2.0), 1.0, 40.0 + math.log1p(math.exp(-40.0)),
+                    math.log1p(math.exp(-40.0)), math.exp(-700.0),
+                    2.5 + math.log1p(math.exp(-2.5))])
+    one = np.ones((1, 1, 1))
+    got = np.empty(v.size)
+    for t in range(v.size):
+        yt, _ = orc.scan(one, v[t].reshape(1, 1, 1), -np.ones((1, 1)), one, one,
+                         delta_softplus=True)
+        got[t] = yt[0, 0, 0]
+    rel = np.abs(got - ref) / np.abs(ref)
+    assert np.all(rel <= 1e-14), ("softplus values", got, ref)
+
+
+# --------------------------------------------------------------------------
+# P11: output gate out = y * silu(z) (p3 "简化的SSM架构": the Mamba block wraps
+#      the SSM in a gated-MLP branch; reading: the gate multiplies the whole
+#      SSM output, skip term included)
+# --------------------------------------------------------------------------
+
+def pin_gate(orc):
+    rng = _rng(111)
+    Bt, L, D, N = 2, 25, 5, 4
+    x, delta, A, B, C, Dsk = _random_problem(rng, Bt, L, D, N)
+    z = rng.normal(0.0, 3.0, (Bt, L, D))
+    z[0, 0, :] = [0.0, -50.0, 50.0, 1e-3, -1e-3]
+    w = rng.standard_normal((D, 3))
+    for zoh in (False, True):
+        for conv in (False, True):
+            kw = dict(D=Dsk, zoh=zoh, conv_w=w if conv else None)
+            y0, h0 = orc.scan(x, delta, A, B, C, **kw)
+            y1, h1 = orc.scan(x, delta, A, B, C, z=z, **kw)
+            _rel_close(y1, y0 * (z * expit(z)), 1e-14, "gate zoh=%s conv=%s" % (zoh, conv))
+            _rel_close(h1, h0, 0.0, "gate leaves the state alone")
+    assert np.all(y1[0, 0, 0] == 0.0)
+
+
+# --------------------------------------------------------------------------
+# P12: conv window carried across calls (p1 "一、Motivation": recurrent
+#      inference needs only the carried state and the new input)
+# --------------------------------------------------------------------------
+
+def pin_conv_state_window(orc):
+    """conv_state_out is the last K-1 raw inputs, oldest first, reaching into
+    conv_state_in when the call is shorter than the window."""
+    rng = _rng(112)
+    Bt, D, N, K = 2, 3, 2, 4
+    S = K - 1
+    w = rng.standard_normal((D, K))
+    st = rng.standard_normal((Bt, D, S))
+    for L in (0, 1, 2, 3, 7):
+        x = rng.standard_normal((Bt, L, D))
+        out = np.full((Bt, D, S), np.nan)
+        orc.scan(x, np.full_like(x, 0.1), -np.ones((D, N)), np.ones((Bt, L, N)),
+                 np.ones((Bt, L, N)), conv_w=w, conv_state_in=st, conv_state_out=out)
+        seq = np.concatenate([st, np.transpose(x, (0, 2, 1))], axis=2)   # (Bt, D, S + L)
+        _rel_close(out, seq[:, :, L:L + S], 0.0, "window L=%d" % L)
+
+
+def pin_conv_state_prefix(orc):
+    """A conv state acts as K-1 extra inputs before token 0: the scan input u
+    with state s equals the u that a zero-state call over [s, x] computes at
+    its last L positions (numpy convolution of the concatenated sequence)."""
+    rng = _rng(113)
+    Bt, L, D = 2, 12, 3
+    for K in (2, 3, 4):
+        x = rng.standard_normal((Bt, L, D))
+        w = rng.standard_normal((D, K))
+        bias = rng.standard_normal(D)
+        st = rng.standard_normal((Bt, D, K - 1))
+        N = 2
+        y, _ = orc.scan(x, np.full_like(x, 0.1), -np.ones((D, N)), np.ones((Bt, L, N)),
+                        np.zeros((Bt, L, N)), D=np.ones(D), conv_w=w, conv_b=bias,
+                        conv_state_in=st)
+        ref = np.zeros((Bt, L, D))
+        for b in range(Bt):
+            for d in range(D):
+                full = np.concatenate([st[b, d], x[b, :, d]])
+                ref[b, :, d] = silu_ref(np.convolve(full, w[d, ::-1])[K - 1:K - 1 + L] + bias[d])
+        _rel_close(y, ref, 1e-13, "state as prefix K=%d" % K)
+
+
+def pin_conv_split_invariance(orc):
+    """scan(x[:cut]) then scan(x[cut:]) with h and the conv window carried
+    equals scan(x), including cuts shorter than the window, with softplus
+    Delta and the gate on."""
+    rng = _rng(114)
+    Bt, L, D, N = 2, 40, 3, 4
+    x, raw, A, B, C, Dsk = _random_problem(rng, Bt, L, D, N)
+    bias = rng.standard_normal(D)
+    z = rng.standard_normal((Bt, L, D))
+    h0 = rng.standard_normal((Bt, D, N))
+    for K in (2, 4):
+        w = rng.standard_normal((D, K))
+        cb = rng.standard_normal(D)
+        st0 = rng.standard_normal((Bt, D, K - 1))
+        kw = dict(D=Dsk, conv_w=w, conv_b=cb, delta_bias=bias, delta_softplus=True, zoh=True)
+        cs_full = np.zeros((Bt, D, K - 1))
+        y_full, h_full = orc.scan(x, raw, A, B, C, h0=h0, z=z, conv_state_in=st0,
+                                  conv_state_out=cs_full, **kw)
+        for cut in (1, 2, 21, 39):
+            sl1, sl2 = slice(0, cut), slice(cut, L)
+            cs1 = np.zeros((Bt, D, K - 1))
+            y1, h1 = orc.scan(x[:, sl1], raw[:, sl1], A, B[:, sl1], C[:, sl1], h0=h0,
+                              z=z[:, sl1], conv_state_in=st0, conv_state_out=cs1, **kw)
+            cs2 = np.zeros((Bt, D, K - 1))
+            y2, h2 = orc.scan(x[:, sl2], raw[:, sl2], A, B[:, sl2], C[:, sl2], h0=h1,
+                              z=z[:, sl2], conv_state_in=cs1, conv_state_out=cs2, **kw)
+            what = "K=%d cut=%d" % (K, cut)
+            _rel_close(np.concatenate([y1, y2], axis=1), y_full, 1e-12, "split y " + what)
+            _rel_close(h2, h_full, 1e-12, "split h " + what)
+            _rel_close(cs2, cs_full, 0.0, "split window " + what)
+
+
+def pin_decode_conv_equals_scan(orc):
+    """Decode steps with the conv window, softplus Delta and the gate equal
+    one scan over the same tokens, for y, h and the window."""
+    rng = _rng(115)
+    Bt, L, D, N, K = 2, 9, 3, 4, 4
+    x, raw, A, B, C, Dsk = _random_problem(rng, Bt, L, D, N)
+    bias = rng.standard_normal(D)
+    z = rng.standard_normal((Bt, L, D))
+    h0 = rng.standard_normal((Bt, D, N))
+    w = rng.standard_normal((D, K))
+    cb = rng.standard_normal(D)
+    st0 = rng.standard_normal((Bt, D, K - 1))
+    for zoh in (False, True):
+        cs_scan = np.zeros((Bt, D, K - 1))
+        y_scan, h_scan = orc.scan(x, raw, A, B, C, D=Dsk, h0=h0, z=z, conv_w=w, conv_b=cb,
+                                  conv_state_in=st0, conv_state_out=cs_scan, zoh=zoh,
+                                  delta_bias=bias, delta_softplus=True)
+        h, cs = h0.copy(), st0.copy()
+        ys = []
+        for t in range(L):
+            yt, h, cs = orc.step(h, x[:, t], raw[:, t], A, B[:, t], C[:, t], D=Dsk, zoh=zoh,
+                                 delta_bias=bias, delta_softplus=True, z=z[:, t], conv_w=w,
+                                 conv_b=cb, conv_state=cs)
+            ys.append(yt)
+        _rel_close(np.stack(ys, axis=1), y_scan, 1e-13, "decode+conv y")
+        _rel_close(h, h_scan, 1e-13, "decode+conv h")
+        _rel_close(cs, cs_scan, 0.0, "decode+conv window")
+
+
 ALL_PINS = [
     pin_hand_expansion_lti, pin_hand_expansion_selective, pin_lti_kernel,
     pin_lti_steady_state, pin_brute_force, pin_split_invariance,
     pin_associative_chunks, pin_prefix_sum, pin_zoh_constant_input, pin_zoh_ode,
     pin_special_cases, pin_decode_equals_scan, pin_conv_identity_tap,
-    pin_conv_numpy, pin_conv_scan_brute,
+    pin_conv_numpy, pin_conv_scan_brute, pin_softplus_delta, pin_softplus_values, pin_gate,
+    pin_conv_state_window, pin_conv_state_prefix, pin_conv_split_invariance,
+    pin_decode_conv_equals_scan,
 ]

@@ -24,8 +24,8 @@ MUTANTS = [
     ("readout_before_update",
      "h[n] = abar * h[n] + bbar * u;\n      acc += Ct[n] * h[n];",
      "acc += Ct[n] * h[n];\n      h[n] = abar * h[n] + bbar * u;"),
-    ("delta_lag", "const double dt = p.delta[(b * L + t) * D + d];",
-     "const double dt = p.delta[(b * L + (t > 0 ? t - 1 : 0)) * D + d];"),
+    ("delta_lag", "double v = p.delta[(b * p.seqlen + t) * p.dim + d];",
+     "double v = p.delta[(b * p.seqlen + (t > 0 ? t - 1 : 0)) * p.dim + d];"),
     ("A_transposed", "const double a_cont = p.A[d * N + n];",
      "const double a_cont = p.A[(n * D + d) % (D * N)];"),
     ("conv_flipped", "const int64_t src = t - (K - 1) + k;", "const int64_t src = t - k;"),
@@ -36,6 +36,19 @@ MUTANTS = [
      "const double* Bt = p.Bm + (b * L + (t > 0 ? t - 1 : 0)) * N;"),
     ("C_from_batch0", "const double* Ct = p.Cm + (b * L + t) * N;",
      "const double* Ct = p.Cm + t * N;"),
+    ("softplus_no_bias", "if (p.delta_bias) v += p.delta_bias[d];", ""),
+    ("softplus_naive", "std::log1p(std::exp(-std::fabs(v)))",
+     "std::log(1.0 + std::exp(-std::fabs(v)))"),
+    ("softplus_sign", "(v > 0.0 ? v : 0.0)", "(v > 0.0 ? 0.0 : v)"),
+    ("gate_before_skip",
+     "double out = acc + dskip * u;\n    if (p.z) out *= silu(p.z[(b * L + t) * D + d]);",
+     "double out = acc;\n    if (p.z) out *= silu(p.z[(b * L + t) * D + d]);\n    out += dskip * u;"),
+    ("gate_sigmoid", "if (p.z) out *= silu(p.z[(b * L + t) * D + d]);",
+     "if (p.z) out *= 1.0 / (1.0 + std::exp(-p.z[(b * L + t) * D + d]));"),
+    ("conv_state_ignored", "if (!p.conv_state_in || t < -S) return 0.0;", "return 0.0;"),
+    ("conv_state_reversed", "return p.conv_state_in[(b * p.dim + d) * S + S + t];",
+     "return p.conv_state_in[(b * p.dim + d) * S - 1 - t];"),
+    ("conv_state_out_shift", "x_at(p, b, L - S + j, d);", "x_at(p, b, L - S + j - 1, d);"),
 ]
 
 
