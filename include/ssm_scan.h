@@ -15,7 +15,18 @@
  * the causal depthwise conv1d + SiLU of x when conv_w is given,
  *
  *   u[b,t,d] = silu(conv_b[d] + sum_{k<K} conv_w[d,k] * x[b, t-K+1+k, d]),
- *   x[b, t<0, d] = 0,   silu(z) = z / (1 + exp(-z)).
+ *   x[b, t<0, d] = conv_state_in[b, d, K-1+t] (0 when conv_state_in is NULL),
+ *   silu(z) = z / (1 + exp(-z)).
+ *
+ * Optional fused steps around the scan:
+ *   - step size from its pre-activation: Delta = delta + delta_bias[d], and
+ *     with delta_softplus Delta = softplus(delta + delta_bias[d]),
+ *     softplus(v) = log(1 + exp(v));
+ *   - output gate: y[b,t,d] is multiplied by silu(z[b,t,d]);
+ *   - conv window across calls: conv_state_out[b, d, j] = x[b, L-K+1+j, d]
+ *     (the last K-1 inputs, oldest first, reaching into conv_state_in when
+ *     L < K-1), so a sequence scanned in pieces, or a prefill followed by
+ *     ssm_step calls, sees the same window as one call.
  *
  * Passages defining each step (web pages on Mamba; section names as printed):
  *   - continuous SSM, ZOH discretization Abar = exp(Delta A),
@@ -34,12 +45,21 @@
  *     "选择性的实现细节" (SelectiveSSM);
  *   - the single-token recurrent step with a cached state (constant cost per
  *     generated token): 53ai.com explainer, section "一、Motivation", and the
- *     datacamp tutorial's complexity table.
+ *     datacamp tutorial's complexity table;
+ *   - Delta = Softplus(Linear(x)), the bias of that projection being
+ *     delta_bias: gsyq.cn section "选择性的数学解析"; VMamba note section
+ *     "mamba：从S4到S6的算法变化流程" (tau_Delta = softplus);
+ *   - the gated block around the SSM (H3 block merged with a gated MLP):
+ *     VMamba note section "简化的SSM架构".  The page's figure with the gate
+ *     formula is lost; y * silu(z), applied after the skip term, is the
+ *     reading taken.
  *
  * Conventions shared by every entry point.
  *   Layout     all arrays are dense, row-major, last dimension fastest:
  *              x, Delta, y (batch, L, D); B, C (batch, L, N); A (D, N);
- *              Dskip, conv_b (D); conv_w (D, K); h0, h_last (batch, D, N).
+ *              Dskip, conv_b, delta_bias (D); conv_w (D, K); h0, h_last
+ *              (batch, D, N); z like x; conv_state_in / conv_state_out
+ *              (batch, D, K-1) fp32, oldest input first.
  *              Base pointers must be aligned to their element size; B and C
  *              rows are read with scalar loads, so B and C base pointers must
  *              be 4-byte aligned and are best 64-byte aligned.
@@ -53,12 +73,14 @@
  *              status says why (ssm_last_error_message() has the detail).  A
  *              failed launch returns SSM_ERR_HIP; faults inside kernels
  *              surface at the caller's next synchronization.
- *   Dtypes     x, Delta, B, C share in_dtype (fp32 or bf16); y has out_dtype;
- *              A, Dskip, conv weights and states are fp32; arithmetic and the
- *              state are fp32; bf16 outputs are rounded to nearest even.
+ *   Dtypes     x, Delta, B, C, z share in_dtype (fp32 or bf16); y has
+ *              out_dtype; A, Dskip, delta_bias, conv weights, conv states and
+ *              h are fp32; arithmetic and the state are fp32; bf16 outputs are
+ *              rounded to nearest even.
  *   Empty      seqlen == 0 or batch * dim == 0 is valid.  With seqlen == 0 and
  *              batch * dim > 0, h_last (if given) receives h0 (zeros if h0 is
- *              NULL) and nothing else is touched.
+ *              NULL), conv_state_out (if given) receives conv_state_in (zeros
+ *              if NULL), and nothing else is touched.
  */
 #ifndef SSM_SCAN_H_
 #define SSM_SCAN_H_
@@ -70,7 +92,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 typedef enum {
   SSM_OK = 0,
@@ -78,7 +100,8 @@ typedef enum {
   SSM_ERR_SHAPE = 2,       /* negative sizes, or byte counts overflow int64 */
   SSM_ERR_DTYPE = 3,       /* unknown dtype or discretization enum value */
   SSM_ERR_UNSUPPORTED = 4, /* dstate not in {1,2,4,8,16}, conv_k not in 1..4,
-                              misaligned pointer, negative chunk_len, reserved != 0 */
+                              misaligned pointer, negative chunk_len, reserved != 0,
+                              delta_softplus not 0/1, conv state without conv_w */
   SSM_ERR_ALIAS = 5,       /* an output overlaps an input or another output */
   SSM_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
   SSM_ERR_HIP = 7          /* the HIP runtime rejected a launch */
@@ -111,6 +134,15 @@ typedef struct {
   int32_t reserved;                   /* must be 0 */
   void* ev_main_start;                /* optional hipEvent_t recorded on hip_stream right */
   void* ev_main_stop;                 /* before / after the output-pass kernel; NULL = none */
+  /* since ABI 2 */
+  const float* delta_bias;            /* (D) or NULL = 0, added to delta */
+  int32_t delta_softplus;             /* 1: Delta = softplus(delta + delta_bias); 0: no softplus */
+  int32_t reserved2;                  /* must be 0 */
+  const void* z;                      /* (Bt, L, D) gate or NULL = no gate: y *= silu(z) */
+  const float* conv_state_in;         /* (Bt, D, K-1) inputs before token 0, or NULL = zeros;
+                                         requires conv_w */
+  float* conv_state_out;              /* (Bt, D, K-1) receives the last K-1 inputs, or NULL;
+                                         requires conv_w; must not overlap any other buffer */
 } ssm_scan_args_t;
 
 typedef struct {
@@ -128,6 +160,15 @@ typedef struct {
   float* h;                           /* (Bt, D, N) cached state, updated in place;
                                          aligned to 4 * min(N, 4) bytes */
   void* y;                            /* (Bt, D) output, read from the updated state */
+  /* since ABI 2 */
+  const float* delta_bias;            /* (D) or NULL = 0, added to delta */
+  int32_t delta_softplus;             /* 1: Delta = softplus(delta + delta_bias) */
+  int32_t conv_k;                     /* taps of the conv (1..4); ignored if conv_w is NULL */
+  const void* z;                      /* (Bt, D) gate or NULL: y *= silu(z) */
+  const float* conv_w;                /* (D, K) or NULL = no conv: u = x */
+  const float* conv_b;                /* (D) or NULL = zero bias */
+  float* conv_state;                  /* (Bt, D, K-1) conv window, updated in place (shifted to
+                                         end with x); required when conv_w is given and K > 1 */
 } ssm_step_args_t;
 
 /* Returns SSM_ABI_VERSION. */
@@ -149,10 +190,12 @@ int64_t ssm_scan_plan_chunk_len(const ssm_scan_args_t* args);
  * which is exact up to floating-point rounding order. */
 ssm_status_t ssm_scan_fwd(const ssm_scan_args_t* args, void* hip_stream);
 
-/* One recurrent decode step per sequence: h <- Abar h + Bbar x, then
- * y = C . h + Dskip * x, with h updated in place.  Same arithmetic as
- * ssm_scan_fwd with seqlen = 1, h0 = h_last = h and no conv prologue.
- * y must not overlap h or any input. */
+/* One recurrent decode step per sequence: u = x (or the conv over the
+ * window conv_state followed by x, then SiLU), h <- Abar h + Bbar u, then
+ * y = (C . h + Dskip * u) (* silu(z)), with h and conv_state updated in
+ * place.  Same arithmetic as ssm_scan_fwd with seqlen = 1, h0 = h_last = h
+ * and conv_state_in = conv_state_out = conv_state.  y must not overlap h,
+ * conv_state or any input. */
 ssm_status_t ssm_step(const ssm_step_args_t* args, void* hip_stream);
 
 /* Static description of a status code. */

@@ -9,10 +9,13 @@ in the library's HIP kernels.  PyTorch supplies device memory and streams.
     y, h_last = scan(x, delta, A, B, C, D=None, h0=None, ...)
     y = step(h, x, delta, A, B, C, D=None, ...)      # h updated in place
 
-Shapes: x, delta (batch, L, dim); A (dim, N); B, C (batch, L, N); D (dim,);
-h0, h_last, h (batch, dim, N); conv_w (dim, K <= 4); conv_b (dim,).
-x, delta, B, C are float32 or bfloat16 (all the same); A, D, states and conv
-weights are float32.
+Shapes: x, delta, z (batch, L, dim); A (dim, N); B, C (batch, L, N); D,
+delta_bias (dim,); h0, h_last, h (batch, dim, N); conv_w (dim, K <= 4);
+conv_b (dim,); conv states (batch, dim, K - 1).  x, delta, B, C, z are
+float32 or bfloat16 (all the same); A, D, delta_bias, states and conv weights
+are float32.  Optional fused steps: delta_softplus (Delta = softplus(delta +
+delta_bias)), the gate z (y * silu(z)) and the conv window carried across
+calls (conv_state_in / conv_state_out for the scan, conv_state for step).
 
 If the library is not built, importing works but every call raises: there is
 no CPU fallback.
@@ -55,6 +58,9 @@ class ScanArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("chunk_len", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("ev_main_start", ctypes.c_void_p), ("ev_main_stop", ctypes.c_void_p),
+        ("delta_bias", ctypes.c_void_p), ("delta_softplus", ctypes.c_int32),
+        ("reserved2", ctypes.c_int32), ("z", ctypes.c_void_p),
+        ("conv_state_in", ctypes.c_void_p), ("conv_state_out", ctypes.c_void_p),
     ]
 
 
@@ -67,6 +73,9 @@ class StepArgs(ctypes.Structure):
         ("x", ctypes.c_void_p), ("delta", ctypes.c_void_p), ("A", ctypes.c_void_p),
         ("Bm", ctypes.c_void_p), ("Cm", ctypes.c_void_p), ("Dskip", ctypes.c_void_p),
         ("h", ctypes.c_void_p), ("y", ctypes.c_void_p),
+        ("delta_bias", ctypes.c_void_p), ("delta_softplus", ctypes.c_int32),
+        ("conv_k", ctypes.c_int32), ("z", ctypes.c_void_p), ("conv_w", ctypes.c_void_p),
+        ("conv_b", ctypes.c_void_p), ("conv_state", ctypes.c_void_p),
     ]
 
 
@@ -165,7 +174,8 @@ def _stream_handle(stream) -> Optional[int]:
 
 
 def make_scan_args(x, delta, A, B, C, D=None, h0=None, h_last=None, y=None, conv_w=None,
-                   conv_b=None, zoh=False, chunk_len=0) -> ScanArgs:
+                   conv_b=None, zoh=False, chunk_len=0, delta_bias=None, delta_softplus=False,
+                   z=None, conv_state_in=None, conv_state_out=None) -> ScanArgs:
     """Fill a ScanArgs from tensors (shape checks are the library's job)."""
     if x.dim() != 3 or A.dim() != 2:
         raise ValueError("x must be (batch, L, dim) and A (dim, N)")
@@ -202,8 +212,27 @@ def make_scan_args(x, delta, A, B, C, D=None, h0=None, h_last=None, y=None, conv
             raise ValueError("conv_b must be (dim,)")
         a.conv_w, a.conv_b = _ptr(_f32(conv_w, "conv_w")), _ptr(_f32(conv_b, "conv_b"))
         a.conv_k = conv_w.shape[1]
+        for name, t in (("conv_state_in", conv_state_in), ("conv_state_out", conv_state_out)):
+            if t is not None and tuple(t.shape) != (batch, dim, a.conv_k - 1):
+                raise ValueError("%s must be (batch, dim, K - 1)" % name)
+    a.conv_state_in = _ptr(_f32(conv_state_in, "conv_state_in"))
+    a.conv_state_out = _ptr(_f32(conv_state_out, "conv_state_out"))
+    _fill_fused(a, dim, delta_bias, delta_softplus, z, tuple(x.shape))
     a.chunk_len = int(chunk_len)
     return a
+
+
+def _fill_fused(a, dim, delta_bias, delta_softplus, z, z_shape):
+    if delta_bias is not None and tuple(delta_bias.shape) != (dim,):
+        raise ValueError("delta_bias must be (dim,)")
+    a.delta_bias = _ptr(_f32(delta_bias, "delta_bias"))
+    a.delta_softplus = 1 if delta_softplus else 0
+    if z is not None:
+        if tuple(z.shape) != z_shape:
+            raise ValueError("z must have the shape of x")
+        if _dtype_code(z) != a.in_dtype:
+            raise ValueError("z must have the dtype of x")
+    a.z = _ptr(z)
 
 
 def workspace_size(args: ScanArgs) -> int:
@@ -220,13 +249,15 @@ def abi_version() -> int:
 
 def scan(x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None, zoh=False,
          out_dtype=None, want_h_last=True, y=None, h_last=None, chunk_len=0,
-         workspace=None, stream=None, events=None) -> Tuple[object, object]:
+         workspace=None, stream=None, events=None, delta_bias=None, delta_softplus=False,
+         z=None, conv_state_in=None, conv_state_out=None) -> Tuple[object, object]:
     """Selective-scan forward on the current (or given) stream.
 
     Returns (y, h_last); h_last is None when want_h_last is False and no
     h_last tensor is passed.  ``workspace`` (uint8 device tensor) may be
     passed to avoid an allocation per call; ``events`` = (start, stop) raw
-    hipEvent_t handles recorded around the output-pass kernel."""
+    hipEvent_t handles recorded around the output-pass kernel.
+    ``conv_state_out`` (float32 (batch, dim, K - 1)) is filled in place."""
     torch = _torch()
     lib = load_library()
     if y is None:
@@ -235,7 +266,8 @@ def scan(x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None, zoh=False
     if h_last is None and want_h_last:
         h_last = torch.empty((x.shape[0], x.shape[2], A.shape[1]), dtype=torch.float32,
                              device=x.device)
-    args = make_scan_args(x, delta, A, B, C, D, h0, h_last, y, conv_w, conv_b, zoh, chunk_len)
+    args = make_scan_args(x, delta, A, B, C, D, h0, h_last, y, conv_w, conv_b, zoh, chunk_len,
+                          delta_bias, delta_softplus, z, conv_state_in, conv_state_out)
     need = int(lib.ssm_scan_workspace_size(ctypes.byref(args)))
     if need > 0:
         if workspace is None or workspace.numel() < need:
@@ -270,7 +302,9 @@ class PreparedScan:
 
 
 def prepare_scan(x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None, zoh=False,
-                 y=None, h_last=None, chunk_len=0, workspace=None, out_dtype=None):
+                 y=None, h_last=None, chunk_len=0, workspace=None, out_dtype=None,
+                 delta_bias=None, delta_softplus=False, z=None, conv_state_in=None,
+                 conv_state_out=None):
     """Allocate outputs and workspace (if not given), check and marshal the
     arguments once; returns (PreparedScan, y, h_last)."""
     torch = _torch()
@@ -278,18 +312,22 @@ def prepare_scan(x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None, z
     if y is None:
         y = torch.empty(x.shape, dtype=out_dtype if out_dtype is not None else x.dtype,
                         device=x.device)
-    args = make_scan_args(x, delta, A, B, C, D, h0, h_last, y, conv_w, conv_b, zoh, chunk_len)
+    args = make_scan_args(x, delta, A, B, C, D, h0, h_last, y, conv_w, conv_b, zoh, chunk_len,
+                          delta_bias, delta_softplus, z, conv_state_in, conv_state_out)
     need = int(lib.ssm_scan_workspace_size(ctypes.byref(args)))
     if need > 0 and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     if need > 0:
         args.workspace = _ptr(workspace)
         args.workspace_bytes = workspace.numel()
-    keep = (x, delta, A, B, C, D, h0, h_last, y, conv_w, conv_b, workspace)
+    keep = (x, delta, A, B, C, D, h0, h_last, y, conv_w, conv_b, workspace, delta_bias, z,
+            conv_state_in, conv_state_out)
     return PreparedScan(args, keep), y, h_last
 
 
-def make_step_args(h, x, delta, A, B, C, D=None, y=None, zoh=False) -> StepArgs:
+def make_step_args(h, x, delta, A, B, C, D=None, y=None, zoh=False, delta_bias=None,
+                   delta_softplus=False, z=None, conv_w=None, conv_b=None,
+                   conv_state=None) -> StepArgs:
     if h.dim() != 3 or x.dim() != 2:
         raise ValueError("h must be (batch, dim, N) and x (batch, dim)")
     batch, dim, N = h.shape
@@ -315,6 +353,17 @@ def make_step_args(h, x, delta, A, B, C, D=None, y=None, zoh=False) -> StepArgs:
     a.Dskip = _ptr(_f32(D, "D"))
     a.h = _ptr(_f32(h, "h"))
     a.y = _ptr(y)
+    _fill_fused(a, dim, delta_bias, delta_softplus, z, (batch, dim))
+    if conv_w is not None:
+        if conv_w.dim() != 2 or conv_w.shape[0] != dim:
+            raise ValueError("conv_w must be (dim, K)")
+        if conv_b is not None and tuple(conv_b.shape) != (dim,):
+            raise ValueError("conv_b must be (dim,)")
+        a.conv_k = conv_w.shape[1]
+        if conv_state is not None and tuple(conv_state.shape) != (batch, dim, a.conv_k - 1):
+            raise ValueError("conv_state must be (batch, dim, K - 1)")
+        a.conv_w, a.conv_b = _ptr(_f32(conv_w, "conv_w")), _ptr(_f32(conv_b, "conv_b"))
+        a.conv_state = _ptr(_f32(conv_state, "conv_state"))
     return a
 
 
@@ -332,25 +381,33 @@ class PreparedStep:
         _raise_for(self._lib, status)
 
 
-def prepare_step(h, x, delta, A, B, C, D=None, zoh=False, y=None, out_dtype=None):
+def prepare_step(h, x, delta, A, B, C, D=None, zoh=False, y=None, out_dtype=None,
+                 delta_bias=None, delta_softplus=False, z=None, conv_w=None, conv_b=None,
+                 conv_state=None):
     """Returns (PreparedStep, y) for repeated launches on the same buffers."""
     torch = _torch()
     if y is None:
         y = torch.empty(x.shape, dtype=out_dtype if out_dtype is not None else x.dtype,
                         device=x.device)
-    args = make_step_args(h, x, delta, A, B, C, D, y, zoh)
-    return PreparedStep(args, (h, x, delta, A, B, C, D, y)), y
+    args = make_step_args(h, x, delta, A, B, C, D, y, zoh, delta_bias, delta_softplus, z,
+                          conv_w, conv_b, conv_state)
+    keep = (h, x, delta, A, B, C, D, y, delta_bias, z, conv_w, conv_b, conv_state)
+    return PreparedStep(args, keep), y
 
 
-def step(h, x, delta, A, B, C, D=None, zoh=False, y=None, out_dtype=None, stream=None):
-    """One decode step; h (float32, (batch, dim, N)) is updated in place.
+def step(h, x, delta, A, B, C, D=None, zoh=False, y=None, out_dtype=None, stream=None,
+         delta_bias=None, delta_softplus=False, z=None, conv_w=None, conv_b=None,
+         conv_state=None):
+    """One decode step; h (float32, (batch, dim, N)) and, with a conv,
+    conv_state (float32, (batch, dim, K - 1)) are updated in place.
     Returns y (batch, dim)."""
     torch = _torch()
     lib = load_library()
     if y is None:
         y = torch.empty(x.shape, dtype=out_dtype if out_dtype is not None else x.dtype,
                         device=x.device)
-    args = make_step_args(h, x, delta, A, B, C, D, y, zoh)
+    args = make_step_args(h, x, delta, A, B, C, D, y, zoh, delta_bias, delta_softplus, z,
+                          conv_w, conv_b, conv_state)
     status = lib.ssm_step(ctypes.byref(args), _stream_handle(stream))
     _raise_for(lib, status)
     return y

@@ -31,6 +31,11 @@
 // The ZOH discretization uses h' = a (h + q) - q with q = u B[n] / A[n], which
 // equals a h + (a - 1) q.
 //
+// Fused around the scan (all optional): the step size from its
+// pre-activation, Delta = softplus(delta + bias[d]), applied as each block of
+// Delta values becomes current; the output gate y * silu(z), z streamed like
+// x; and the conv window taken from / handed back to a caller's conv state.
+//
 // Slow decay.  When |Delta A| is tiny, Abar = exp(Delta A) lies so close to 1
 // that rounding it to fp32 biases the decay rate by up to 2^-24 / |Delta A|,
 // and with a steady Delta that bias compounds over the whole memory horizon.
@@ -77,7 +82,15 @@ struct ScanParams {
   int32_t conv_k;
   int32_t nwg;           // workgroups in the launch (for the XCD remap)
   float exact_thr;       // min |Delta A| below this takes the slow-decay form
+  const float* dt_bias;  // (D) or null
+  int32_t dt_mode;       // kDtRaw, kDtBias or kDtSoftplus
+  const void* z;         // (Bt, L, D) gate or null
+  const float* cs_in;    // (Bt, D, conv_k - 1) conv window before token 0, or null
+  float* cs_out;         // (Bt, D, conv_k - 1) last conv_k - 1 inputs, or null
 };
+
+// How the step size is formed from the given delta values.
+enum DtMode : int { kDtRaw = 0, kDtBias = 1, kDtSoftplus = 2 };
 
 struct StepParams {
   const void* x;
@@ -92,6 +105,13 @@ struct StepParams {
   int32_t dtiles;
   int32_t nwg;
   float exact_thr;
+  const float* dt_bias;
+  int32_t dt_mode;
+  int32_t conv_k;        // 0 = no conv
+  const void* z;         // (Bt, D) gate or null
+  const float* conv_w;   // (D, conv_k)
+  const float* conv_b;
+  float* conv_state;     // (Bt, D, conv_k - 1), updated in place
 };
 
 // ---------------------------------------------------------------------------
@@ -144,6 +164,24 @@ __device__ __forceinline__ float silu(float z) {
   // z / (1 + exp(-z)); for z -> -inf the exp overflows to inf and rcp gives 0
   const float e = exp2_fast(-z * kLog2e);
   return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// softplus(v) = log(1 + exp(v)) = max(v, 0) + log1p(e), e = exp(-|v|) in
+// (0, 1].  log1p(e) is taken as log(w) * e / (w - 1) with w = 1 + e rounded
+// (Goldberg's correction for the rounding of w), and as e itself once w
+// rounds to 1, so the result keeps full relative precision far into the
+// negative tail, where softplus(v) ~ exp(v).
+__device__ __forceinline__ float softplus(float v) {
+  const float e = exp2_fast(-fabsf(v) * kLog2e);
+  const float w = 1.0f + e;
+  const float l = (w == 1.0f) ? e : (__builtin_amdgcn_logf(w) * kLn2) * (e / (w - 1.0f));
+  return fmaxf(v, 0.0f) + l;
+}
+
+// The step size from a given delta value and the channel's bias.
+__device__ __forceinline__ float dt_transform(float v, float bias, int mode) {
+  v += bias;
+  return mode == kDtSoftplus ? softplus(v) : v;
 }
 
 // Workgroups are handed to the 8 XCDs round-robin (id i on XCD i % 8).  Map
@@ -255,9 +293,27 @@ __device__ __forceinline__ void conv_init(ConvState& cs, const ScanParams& p, in
   cs.bias = p.conv_b ? p.conv_b[d] : 0.0f;
   const InT* xp = static_cast<const InT*>(p.x);
   const int64_t base = b * p.L;
-  cs.xm3 = (t0 >= 3) ? ld(xp + (base + t0 - 3) * p.D + d) : 0.0f;
-  cs.xm2 = (t0 >= 2) ? ld(xp + (base + t0 - 2) * p.D + d) : 0.0f;
-  cs.xm1 = (t0 >= 1) ? ld(xp + (base + t0 - 1) * p.D + d) : 0.0f;
+  // x[t] for t = t0 - 3 .. t0 - 1; before token 0 from the caller's window
+  // (x[-S .. -1] = cs_in[b, d, 0 .. S-1]), or zero
+  const int S = K - 1;
+  const float* win = p.cs_in ? p.cs_in + (b * p.D + d) * S : nullptr;
+  float xm[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int64_t t = t0 - 3 + k;
+    if (t >= 0) xm[k] = ld(xp + (base + t) * p.D + d);
+    else xm[k] = (win && t >= -S) ? win[S + t] : 0.0f;
+  }
+  cs.xm3 = xm[0];
+  cs.xm2 = xm[1];
+  cs.xm1 = xm[2];
+}
+
+// The last K - 1 inputs of the window, oldest first, into out[0 .. K-2].
+__device__ __forceinline__ void conv_save(const ConvState& cs, int K, float* out) {
+  const float xm[3] = {cs.xm3, cs.xm2, cs.xm1};
+  const int S = K - 1;
+  for (int j = 0; j < S; ++j) out[j] = xm[3 - S + j];
 }
 
 __device__ __forceinline__ float conv_push(ConvState& cs, float xv) {
@@ -346,15 +402,22 @@ __device__ __forceinline__ void stb(__amdgpu_buffer_rsrc_t r, uint32_t voff, uin
 // arithmetic covers their latency.  (Scalar loads complete out of order, so
 // the only usable wait is "all outstanding"; it falls at the top of the next
 // step, after the loads had a full step to land.)
-template <int N, typename InT, typename OutT, int DISC, bool CONV, bool OUT>
+//
+// GATE (output pass only) streams z like x and multiplies each output by
+// silu(z).  cs_save, when not null, receives the conv window after the last
+// step (the caller passes it for the final chunk only).
+template <int N, typename InT, typename OutT, int DISC, bool CONV, bool OUT, bool GATE>
 __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64_t dbase,
                                            uint32_t lo, int64_t t0, int32_t steps, float (&h)[N],
-                                           float* dsum_out) {
+                                           float* dsum_out, float* cs_save) {
+  static_assert(OUT || !GATE, "the gate applies to the output pass");
   constexpr int kU = OUT ? kUnrollOut : kUnrollSum;
   const int64_t d = dbase + lo;
   ChanConst<N, DISC> cc;
   load_chan<N, DISC>(cc, p.A + d * N, p.exact_thr);
   const float dsk = (OUT && p.Dskip) ? p.Dskip[d] : 0.0f;
+  const int dtm = p.dt_mode;
+  const float dtb = (dtm != kDtRaw && p.dt_bias) ? p.dt_bias[d] : 0.0f;
   ConvState cs;
   if constexpr (CONV) conv_init<InT>(cs, p, b, d, t0);
 
@@ -369,6 +432,8 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const InT*>(p.x) + chunk_base, span_in);
   const __amdgpu_buffer_rsrc_t rd =
       make_rsrc(static_cast<const InT*>(p.delta) + chunk_base, span_in);
+  const __amdgpu_buffer_rsrc_t rz =
+      make_rsrc(static_cast<const InT*>(GATE ? p.z : p.x) + chunk_base, GATE ? span_in : 0u);
   const uint32_t row_out = static_cast<uint32_t>(D * sizeof(OutT));
   // (the summary pass writes no y: its descriptor then covers nothing)
   const __amdgpu_buffer_rsrc_t ry =
@@ -387,8 +452,8 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
   load_row<N>(Bb0, Brow);
   if constexpr (OUT) load_row<N>(Cb0, Crow);
 
-  auto one_step = [&](float xv, float dv, bool has_next, float (&Bcur)[N], float (&Bnext)[N],
-                      float (&Ccur)[N], float (&Cnext)[N]) {
+  auto one_step = [&](float xv, float dv, float zv, bool has_next, float (&Bcur)[N],
+                      float (&Bnext)[N], float (&Ccur)[N], float (&Cnext)[N]) {
     // on the last step re-read the current row instead of running past the end
     const int64_t adv = has_next ? N : 0;
     const InT* nb = Brow + adv;
@@ -410,7 +475,9 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
     const float u = CONV ? conv_push(cs, xv) : xv;
     if constexpr (OUT) {
       const float acc = ssm_step_any<N, DISC, true>(h, cc, Bcur, Ccur, u, dv);
-      stb(ry, lo_out, soff_out, fmaf(dsk, u, acc), static_cast<OutT*>(nullptr));
+      float yv = fmaf(dsk, u, acc);
+      if constexpr (GATE) yv *= silu(zv);
+      stb(ry, lo_out, soff_out, yv, static_cast<OutT*>(nullptr));
       soff_out += row_out;
     } else {
       ssm_step_any<N, DISC, false>(h, cc, Bcur, Bcur, u, dv);
@@ -433,31 +500,39 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
 
   static_assert(kU % 2 == 0, "row buffers alternate within a block");
   const int32_t nblk = steps / kU;
-  float xc[kU], dc[kU];
+  float xc[kU], dc[kU], zc[kU];
   constexpr InT* kIn = nullptr;
   if (nblk > 0) {
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
       xc[j] = ldb(rx, lo_in, j * row_in, kIn);
       dc[j] = ldb(rd, lo_in, j * row_in, kIn);
+      zc[j] = GATE ? ldb(rz, lo_in, j * row_in, kIn) : 0.0f;
     }
   }
   for (int32_t blk = 0; blk < nblk; ++blk) {
-    // Prefetch the next block's x / Delta.  The loads are unconditional (the
-    // last block re-reads its own rows) so that the number of loads in flight
-    // is the same on every path and each wait covers only the older loads.
-    float xn[kU], dn[kU];
+    // Prefetch the next block's x / Delta (/ z).  The loads are unconditional
+    // (the last block re-reads its own rows) so that the number of loads in
+    // flight is the same on every path and each wait covers only the older
+    // loads.
+    float xn[kU], dn[kU], zn[kU];
     const uint32_t nsoff = soff_in + ((blk + 1 < nblk) ? kU * row_in : 0u);
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
       xn[j] = ldb(rx, lo_in, nsoff + j * row_in, kIn);
       dn[j] = ldb(rd, lo_in, nsoff + j * row_in, kIn);
+      zn[j] = GATE ? ldb(rz, lo_in, nsoff + j * row_in, kIn) : 0.0f;
+    }
+    // the block's step sizes from their pre-activations (wave-uniform branch)
+    if (dtm != kDtRaw) {
+#pragma unroll
+      for (int j = 0; j < kU; ++j) dc[j] = dt_transform(dc[j], dtb, dtm);
     }
     const int32_t tb = blk * kU;
 #pragma unroll
     for (int j = 0; j < kU; j += 2) {
-      one_step(xc[j], dc[j], tb + j + 1 < steps, Bb0, Bb1, Cb0, Cb1);
-      one_step(xc[j + 1], dc[j + 1], tb + j + 2 < steps, Bb1, Bb0, Cb1, Cb0);
+      one_step(xc[j], dc[j], zc[j], tb + j + 1 < steps, Bb0, Bb1, Cb0, Cb1);
+      one_step(xc[j + 1], dc[j + 1], zc[j + 1], tb + j + 2 < steps, Bb1, Bb0, Cb1, Cb0);
     }
     if constexpr (!OUT) {
       float bs = dc[0];
@@ -467,13 +542,15 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
     }
     soff_in += kU * row_in;
 #pragma unroll
-    for (int j = 0; j < kU; ++j) { xc[j] = xn[j]; dc[j] = dn[j]; }
+    for (int j = 0; j < kU; ++j) { xc[j] = xn[j]; dc[j] = dn[j]; zc[j] = zn[j]; }
   }
   // remainder (fewer than kU steps); the current rows are in Bb0 / Cb0
   for (int32_t t = nblk * kU; t < steps; ++t) {
     const float xv = ldb(rx, lo_in, soff_in, kIn);
-    const float dv = ldb(rd, lo_in, soff_in, kIn);
-    one_step(xv, dv, t + 1 < steps, Bb0, Bb1, Cb0, Cb1);
+    float dv = ldb(rd, lo_in, soff_in, kIn);
+    const float zv = GATE ? ldb(rz, lo_in, soff_in, kIn) : 0.0f;
+    if (dtm != kDtRaw) dv = dt_transform(dv, dtb, dtm);
+    one_step(xv, dv, zv, t + 1 < steps, Bb0, Bb1, Cb0, Cb1);
     if constexpr (!OUT) sum_add(dv);
 #pragma unroll
     for (int n = 0; n < N; ++n) {
@@ -483,6 +560,9 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
     soff_in += row_in;
   }
   if (!OUT && dsum_out) *dsum_out = dacc - dcomp;
+  if constexpr (CONV && OUT) {
+    if (cs_save) conv_save(cs, p.conv_k, cs_save);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -504,8 +584,8 @@ __global__ void __launch_bounds__(kWave) k_chunk_summary(const ScanParams p) {
 #pragma unroll
   for (int n = 0; n < N; ++n) h[n] = 0.0f;
   const int64_t slot = tl.b * (p.C - 1) + tl.chunk;
-  chunk_loop<N, InT, float, DISC, CONV, false>(p, tl.b, dbase, lo, t0, steps, h,
-                                               p.dsum + slot * p.D + d);
+  chunk_loop<N, InT, float, DISC, CONV, false, false>(p, tl.b, dbase, lo, t0, steps, h,
+                                                      p.dsum + slot * p.D + d, nullptr);
   float* hs = p.hsum + (slot * p.D + d) * N;
 #pragma unroll
   for (int n = 0; n < N; ++n) hs[n] = h[n];
@@ -556,7 +636,7 @@ __global__ void __launch_bounds__(kWave) k_carry_combine(const ScanParams p) {
 
 // Pass 3 (or the only pass): scan each chunk from its carry-in, write y, and
 // h_last from the final chunk.
-template <int N, typename InT, typename OutT, int DISC, bool CONV>
+template <int N, typename InT, typename OutT, int DISC, bool CONV, bool GATE>
 __global__ void __launch_bounds__(kWave) k_scan_out(const ScanParams p) {
   const int wg = xcd_remap(blockIdx.x, p.nwg);
   const Tile tl = tile_of(wg, p.dtiles, p.C);
@@ -580,8 +660,13 @@ __global__ void __launch_bounds__(kWave) k_scan_out(const ScanParams p) {
 #pragma unroll
     for (int n = 0; n < N; ++n) h[n] = cin[n];
   }
-  chunk_loop<N, InT, OutT, DISC, CONV, true>(p, tl.b, dbase, lo, t0, steps, h, nullptr);
-  if (p.h_last && tl.chunk == p.C - 1) {
+  const bool last = tl.chunk == p.C - 1;
+  float* cs_save = (CONV && last && p.cs_out && p.conv_k > 1)
+                       ? p.cs_out + (tl.b * p.D + d) * (p.conv_k - 1)
+                       : nullptr;
+  chunk_loop<N, InT, OutT, DISC, CONV, true, GATE>(p, tl.b, dbase, lo, t0, steps, h, nullptr,
+                                                   cs_save);
+  if (p.h_last && last) {
     float* hl = p.h_last + (tl.b * p.D + d) * N;
 #pragma unroll
     for (int n = 0; n < N; ++n) hl[n] = h[n];
@@ -645,7 +730,8 @@ __device__ __forceinline__ void store_state(float* p, const float (&h)[NL]) {
 // channels of ROWS consecutive batch rows (a row past the batch is skipped,
 // uniformly for the wave).  Lanes past the last channel duplicate channel
 // D - 1: they read the same old state in the same load instruction and store
-// identical values.
+// identical values.  The optional conv window, step-size transform and gate
+// are wave-uniform branches (this kernel is bound by the state traffic).
 template <int N, typename InT, typename OutT, int DISC>
 __global__ void __launch_bounds__(kWave) k_step(const StepParams p) {
   constexpr int NL = StepLayout<N>::NL, S = StepLayout<N>::S, CPW = StepLayout<N>::CPW;
@@ -661,6 +747,17 @@ __global__ void __launch_bounds__(kWave) k_step(const StepParams p) {
   ChanConst<NL, DISC> cc;
   load_chan<NL, DISC>(cc, p.A + d * N + n0, p.exact_thr);
   const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
+  const int dtm = p.dt_mode;
+  const float dtb = (dtm != kDtRaw && p.dt_bias) ? p.dt_bias[d] : 0.0f;
+  // conv taps, zero-padded at the oldest end as in the scan's prologue
+  const int K = p.conv_k;
+  const int SW = K > 0 ? K - 1 : 0;   // window length
+  float cw[kConvTaps] = {0.f, 0.f, 0.f, 0.f};
+  float cb = 0.0f;
+  if (K > 0) {
+    for (int k = 0; k < K; ++k) cw[kConvTaps - K + k] = p.conv_w[d * K + k];
+    cb = p.conv_b ? p.conv_b[d] : 0.0f;
+  }
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     const int64_t b = bt * ROWS + r;
@@ -676,13 +773,35 @@ __global__ void __launch_bounds__(kWave) k_step(const StepParams p) {
       Bv[n] = ld(Bp + n);
       Cv[n] = ld(Cp + n);
     }
-    const float u = ld(static_cast<const InT*>(p.x) + b * p.D + d);
-    const float dv = ld(static_cast<const InT*>(p.delta) + b * p.D + d);
+    float u = ld(static_cast<const InT*>(p.x) + b * p.D + d);
+    float dv = ld(static_cast<const InT*>(p.delta) + b * p.D + d);
+    if (dtm != kDtRaw) dv = dt_transform(dv, dtb, dtm);
+    if (K > 0) {
+      // window x[-SW .. -1] (oldest first), then the new input
+      float* win = p.conv_state + (b * p.D + d) * SW;
+      float xm[3] = {0.f, 0.f, 0.f};
+      for (int k = 0; k < SW; ++k) xm[3 - SW + k] = win[k];
+      float zc = fmaf(cw[3], u, cb);
+      zc = fmaf(cw[2], xm[2], zc);
+      zc = fmaf(cw[1], xm[1], zc);
+      zc = fmaf(cw[0], xm[0], zc);
+      // the window moves on by one input (written by one lane per channel,
+      // after every lane of the wave has read it in the loads above)
+      if (j == 0 && SW > 0) {
+        for (int k = 0; k + 1 < SW; ++k) win[k] = xm[3 - SW + k + 1];
+        win[SW - 1] = u;
+      }
+      u = silu(zc);
+    }
     float acc = ssm_step_any<NL, DISC, true>(h, cc, Bv, Cv, u, dv);
     if constexpr (S >= 2) acc += dpp_quad_xor1(acc);
     if constexpr (S >= 4) acc += dpp_quad_xor2(acc);
     store_state<NL>(hp, h);
-    if (j == 0) st(static_cast<OutT*>(p.y) + b * p.D + d, fmaf(dsk, u, acc));
+    if (j == 0) {
+      float yv = fmaf(dsk, u, acc);
+      if (p.z) yv *= silu(ld(static_cast<const InT*>(p.z) + b * p.D + d));
+      st(static_cast<OutT*>(p.y) + b * p.D + d, yv);
+    }
   }
 }
 

@@ -117,20 +117,34 @@ ssm_status_t check_scan(const ssm_scan_args_t* a, Plan* plan) {
   if (a->conv_w && (a->conv_k < 1 || a->conv_k > ssmk::kConvTaps))
     return fail(SSM_ERR_UNSUPPORTED, "conv_k %d not in 1..4", a->conv_k);
   if (a->chunk_len < 0) return fail(SSM_ERR_UNSUPPORTED, "chunk_len must be >= 0");
-  if (a->reserved != 0) return fail(SSM_ERR_UNSUPPORTED, "reserved field must be 0");
+  if (a->reserved != 0 || a->reserved2 != 0)
+    return fail(SSM_ERR_UNSUPPORTED, "reserved fields must be 0");
+  if (a->delta_softplus != 0 && a->delta_softplus != 1)
+    return fail(SSM_ERR_UNSUPPORTED, "delta_softplus must be 0 or 1");
+  if (!a->conv_w && (a->conv_state_in || a->conv_state_out))
+    return fail(SSM_ERR_UNSUPPORTED, "conv_state_in / conv_state_out need conv_w");
   // byte counts must fit in int64 (and the grid in a launch)
-  int64_t bl, bld, bln, dn, bdn;
+  int64_t bl, bld, bln, dn, bdn, bds;
+  const int64_t win = a->conv_w ? a->conv_k - 1 : 0;
   if (!mul_ok(a->batch, a->seqlen, &bl) || !mul_ok(bl, a->dim, &bld) ||
       !mul_ok(bl, a->dstate, &bln) || !mul_ok(a->dim, a->dstate, &dn) ||
       !mul_ok(a->batch, dn, &bdn) || bld > INT64_MAX / 8 || bln > INT64_MAX / 8 ||
-      bdn > INT64_MAX / 8)
+      bdn > INT64_MAX / 8 || !mul_ok(a->batch * a->dim, win, &bds) || bds > INT64_MAX / 8)
     return fail(SSM_ERR_SHAPE, "sizes overflow");
   *plan = make_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len);
+  const Range cso{win > 0 ? a->conv_state_out : nullptr, size_t(bds) * 4};
+  const Range csi{win > 0 ? a->conv_state_in : nullptr, size_t(bds) * 4};
+  if (misaligned(a->conv_state_in, 4) || misaligned(a->conv_state_out, 4))
+    return fail(SSM_ERR_UNSUPPORTED, "misaligned conv state (4 bytes)");
   if (a->seqlen == 0 || a->batch * a->dim == 0) {
-    // only h_last may be written (with h0 or zeros)
-    if (a->batch * a->dim > 0 && a->h_last && a->h0 &&
-        overlap({a->h_last, size_t(bdn) * 4}, {a->h0, size_t(bdn) * 4}))
-      return fail(SSM_ERR_ALIAS, "h_last overlaps h0");
+    // only h_last (with h0 or zeros) and conv_state_out (with conv_state_in or
+    // zeros) may be written
+    if (a->batch * a->dim > 0) {
+      const Range hl{a->h_last, size_t(bdn) * 4}, h0{a->h0, size_t(bdn) * 4};
+      if (overlap(hl, h0) || overlap(hl, csi) || overlap(hl, cso) || overlap(cso, csi) ||
+          overlap(cso, h0))
+        return fail(SSM_ERR_ALIAS, "an output overlaps another buffer");
+    }
     return SSM_OK;
   }
   if (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->y)
@@ -139,7 +153,8 @@ ssm_status_t check_scan(const ssm_scan_args_t* a, Plan* plan) {
   if (misaligned(a->x, in_sz) || misaligned(a->delta, in_sz) || misaligned(a->Bm, 4) ||
       misaligned(a->Cm, 4) || misaligned(a->y, out_sz) || misaligned(a->A, 4) ||
       misaligned(a->Dskip, 4) || misaligned(a->h0, 4) || misaligned(a->h_last, 4) ||
-      misaligned(a->conv_w, 4) || misaligned(a->conv_b, 4) || misaligned(a->workspace, 256))
+      misaligned(a->conv_w, 4) || misaligned(a->conv_b, 4) || misaligned(a->workspace, 256) ||
+      misaligned(a->z, in_sz) || misaligned(a->delta_bias, 4))
     return fail(SSM_ERR_UNSUPPORTED,
                 "misaligned pointer (element alignment; B, C 4 bytes; workspace 256 bytes)");
   const Range y{a->y, size_t(bld) * out_sz};
@@ -150,12 +165,17 @@ ssm_status_t check_scan(const ssm_scan_args_t* a, Plan* plan) {
       {a->Cm, size_t(bln) * in_sz},       {a->Dskip, size_t(a->dim) * 4},
       {a->h0, size_t(bdn) * 4},           {a->conv_w, size_t(a->dim) * size_t(std::max(a->conv_k, 0)) * 4},
       {a->conv_b, a->conv_w ? size_t(a->dim) * 4 : 0},
+      {a->delta_bias, size_t(a->dim) * 4}, {a->z, size_t(bld) * in_sz},
+      csi,
   };
   for (const Range& r : ins) {
     if (overlap(y, r)) return fail(SSM_ERR_ALIAS, "y overlaps an input");
     if (overlap(hl, r)) return fail(SSM_ERR_ALIAS, "h_last overlaps an input");
+    if (overlap(cso, r)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps an input");
   }
   if (overlap(y, hl)) return fail(SSM_ERR_ALIAS, "y overlaps h_last");
+  if (overlap(y, cso) || overlap(hl, cso))
+    return fail(SSM_ERR_ALIAS, "conv_state_out overlaps an output");
   if (plan->ws_total > 0) {
     if (!a->workspace) return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required", plan->ws_total);
     if (a->workspace_bytes < plan->ws_total)
@@ -164,7 +184,8 @@ ssm_status_t check_scan(const ssm_scan_args_t* a, Plan* plan) {
     const Range ws{a->workspace, plan->ws_total};
     for (const Range& r : ins)
       if (overlap(ws, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps an input");
-    if (overlap(ws, y) || overlap(ws, hl)) return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
+    if (overlap(ws, y) || overlap(ws, hl) || overlap(ws, cso))
+      return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
   }
   const int64_t grid_out = a->batch * plan->C * plan->dtiles;
   if (grid_out > kMaxGrid || (a->batch * a->dim * a->dstate + 63) / 64 > kMaxGrid)
@@ -187,29 +208,45 @@ ssm_status_t check_step(const ssm_step_args_t* a) {
   if (!supported_n(a->dstate))
     return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not in {1,2,4,8,16}", (long long)a->dstate);
   if (a->reserved != 0) return fail(SSM_ERR_UNSUPPORTED, "reserved field must be 0");
-  int64_t bd, dn, bdn, bn;
+  if (a->delta_softplus != 0 && a->delta_softplus != 1)
+    return fail(SSM_ERR_UNSUPPORTED, "delta_softplus must be 0 or 1");
+  if (a->conv_w && (a->conv_k < 1 || a->conv_k > ssmk::kConvTaps))
+    return fail(SSM_ERR_UNSUPPORTED, "conv_k %d not in 1..4", a->conv_k);
+  const int64_t win = a->conv_w ? a->conv_k - 1 : 0;
+  int64_t bd, dn, bdn, bn, bds;
   if (!mul_ok(a->batch, a->dim, &bd) || !mul_ok(a->dim, a->dstate, &dn) ||
-      !mul_ok(a->batch, dn, &bdn) || !mul_ok(a->batch, a->dstate, &bn) || bdn > INT64_MAX / 8)
+      !mul_ok(a->batch, dn, &bdn) || !mul_ok(a->batch, a->dstate, &bn) || bdn > INT64_MAX / 8 ||
+      !mul_ok(bd, win, &bds) || bds > INT64_MAX / 8)
     return fail(SSM_ERR_SHAPE, "sizes overflow");
   if (bd == 0) return SSM_OK;
   if (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->h || !a->y)
     return fail(SSM_ERR_NULL, "x, delta, A, Bm, Cm, h and y are required");
+  if (win > 0 && !a->conv_state)
+    return fail(SSM_ERR_NULL, "conv_state is required with a conv of more than one tap");
   const size_t in_sz = dtype_size(a->in_dtype), out_sz = dtype_size(a->out_dtype);
   if (misaligned(a->x, in_sz) || misaligned(a->delta, in_sz) || misaligned(a->Bm, 4) ||
       misaligned(a->Cm, 4) || misaligned(a->y, out_sz) || misaligned(a->A, 4) ||
-      misaligned(a->Dskip, 4) || misaligned(a->h, 4 * size_t(std::min<int64_t>(a->dstate, 4))))
+      misaligned(a->Dskip, 4) || misaligned(a->h, 4 * size_t(std::min<int64_t>(a->dstate, 4))) ||
+      misaligned(a->z, in_sz) || misaligned(a->delta_bias, 4) || misaligned(a->conv_w, 4) ||
+      misaligned(a->conv_b, 4) || misaligned(a->conv_state, 4))
     return fail(SSM_ERR_UNSUPPORTED,
                 "misaligned pointer (element alignment; B, C 4 bytes; h 4 * min(N, 4) bytes)");
   const Range y{a->y, size_t(bd) * out_sz};
   const Range h{a->h, size_t(bdn) * 4};
-  const Range ins[] = {{a->x, size_t(bd) * in_sz}, {a->delta, size_t(bd) * in_sz},
-                       {a->A, size_t(dn) * 4},     {a->Bm, size_t(bn) * in_sz},
-                       {a->Cm, size_t(bn) * in_sz}, {a->Dskip, size_t(a->dim) * 4}};
+  const Range cs{win > 0 ? a->conv_state : nullptr, size_t(bds) * 4};
+  const Range ins[] = {{a->x, size_t(bd) * in_sz},     {a->delta, size_t(bd) * in_sz},
+                       {a->A, size_t(dn) * 4},         {a->Bm, size_t(bn) * in_sz},
+                       {a->Cm, size_t(bn) * in_sz},    {a->Dskip, size_t(a->dim) * 4},
+                       {a->z, size_t(bd) * in_sz},     {a->delta_bias, size_t(a->dim) * 4},
+                       {a->conv_w, a->conv_w ? size_t(a->dim) * size_t(a->conv_k) * 4 : 0},
+                       {a->conv_b, a->conv_w ? size_t(a->dim) * 4 : 0}};
   for (const Range& r : ins) {
     if (overlap(y, r)) return fail(SSM_ERR_ALIAS, "y overlaps an input");
     if (overlap(h, r)) return fail(SSM_ERR_ALIAS, "h overlaps an input");
+    if (overlap(cs, r)) return fail(SSM_ERR_ALIAS, "conv_state overlaps an input");
   }
   if (overlap(y, h)) return fail(SSM_ERR_ALIAS, "y overlaps h");
+  if (overlap(y, cs) || overlap(h, cs)) return fail(SSM_ERR_ALIAS, "conv_state overlaps an output");
   if ((a->batch * ((a->dim + 15) / 16)) > kMaxGrid) return fail(SSM_ERR_SHAPE, "problem too large");
   return SSM_OK;
 }
@@ -230,7 +267,7 @@ ssm_status_t launch_status(const char* what) {
   return SSM_OK;
 }
 
-template <int N, typename InT, typename OutT, int DISC, bool CONV>
+template <int N, typename InT, typename OutT, int DISC, bool CONV, bool GATE>
 ssm_status_t run_scan(ssmk::ScanParams kp, const Plan& pl, hipStream_t s, hipEvent_t ev0,
                       hipEvent_t ev1) {
   if (pl.C > 1) {
@@ -245,8 +282,8 @@ ssm_status_t run_scan(ssmk::ScanParams kp, const Plan& pl, hipStream_t s, hipEve
   }
   kp.nwg = int32_t(kp.Bt * pl.C * pl.dtiles);
   if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return fail(SSM_ERR_HIP, "hipEventRecord failed");
-  hipLaunchKernelGGL((ssmk::k_scan_out<N, InT, OutT, DISC, CONV>), dim3(kp.nwg), dim3(ssmk::kWave), 0,
-                     s, kp);
+  hipLaunchKernelGGL((ssmk::k_scan_out<N, InT, OutT, DISC, CONV, GATE>), dim3(kp.nwg),
+                     dim3(ssmk::kWave), 0, s, kp);
   if (ssm_status_t st = launch_status("k_scan_out")) return st;
   if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return fail(SSM_ERR_HIP, "hipEventRecord failed");
   return SSM_OK;
@@ -258,11 +295,25 @@ ssm_status_t dispatch_disc(const ssm_scan_args_t* a, const ssmk::ScanParams& kp,
   hipEvent_t e0 = static_cast<hipEvent_t>(a->ev_main_start);
   hipEvent_t e1 = static_cast<hipEvent_t>(a->ev_main_stop);
   const bool conv = a->conv_w != nullptr;
-  if (a->disc == SSM_DISC_ZOH)
-    return conv ? run_scan<N, InT, OutT, ssmk::kZoh, true>(kp, pl, s, e0, e1)
-                : run_scan<N, InT, OutT, ssmk::kZoh, false>(kp, pl, s, e0, e1);
-  return conv ? run_scan<N, InT, OutT, ssmk::kDeltaB, true>(kp, pl, s, e0, e1)
-              : run_scan<N, InT, OutT, ssmk::kDeltaB, false>(kp, pl, s, e0, e1);
+  const bool gate = a->z != nullptr;
+  using namespace ssmk;
+  if (a->disc == SSM_DISC_ZOH) {
+    if (gate)
+      return conv ? run_scan<N, InT, OutT, kZoh, true, true>(kp, pl, s, e0, e1)
+                  : run_scan<N, InT, OutT, kZoh, false, true>(kp, pl, s, e0, e1);
+    return conv ? run_scan<N, InT, OutT, kZoh, true, false>(kp, pl, s, e0, e1)
+                : run_scan<N, InT, OutT, kZoh, false, false>(kp, pl, s, e0, e1);
+  }
+  if (gate)
+    return conv ? run_scan<N, InT, OutT, kDeltaB, true, true>(kp, pl, s, e0, e1)
+                : run_scan<N, InT, OutT, kDeltaB, false, true>(kp, pl, s, e0, e1);
+  return conv ? run_scan<N, InT, OutT, kDeltaB, true, false>(kp, pl, s, e0, e1)
+              : run_scan<N, InT, OutT, kDeltaB, false, false>(kp, pl, s, e0, e1);
+}
+
+int32_t dt_mode_of(const float* bias, int32_t softplus) {
+  if (softplus) return ssmk::kDtSoftplus;
+  return bias ? ssmk::kDtBias : ssmk::kDtRaw;
 }
 
 template <int N>
@@ -333,11 +384,19 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_args_t* a, void* hip_stream) {
   const int64_t BD = a->batch * a->dim;
   if (BD == 0) return SSM_OK;
   if (a->seqlen == 0) {
-    if (!a->h_last) return SSM_OK;
-    const int64_t n = BD * a->dstate;
-    hipLaunchKernelGGL(ssmk::k_state_copy, dim3(uint32_t((n + 255) / 256)), dim3(256), 0, s,
-                       a->h_last, a->h0, n);
-    return launch_status("k_state_copy");
+    if (a->h_last) {
+      const int64_t n = BD * a->dstate;
+      hipLaunchKernelGGL(ssmk::k_state_copy, dim3(uint32_t((n + 255) / 256)), dim3(256), 0, s,
+                         a->h_last, a->h0, n);
+      if (ssm_status_t st = launch_status("k_state_copy")) return st;
+    }
+    if (a->conv_w && a->conv_state_out && a->conv_k > 1) {
+      const int64_t n = BD * (a->conv_k - 1);
+      hipLaunchKernelGGL(ssmk::k_state_copy, dim3(uint32_t((n + 255) / 256)), dim3(256), 0, s,
+                         a->conv_state_out, a->conv_state_in, n);
+      if (ssm_status_t st = launch_status("k_state_copy")) return st;
+    }
+    return SSM_OK;
   }
   ssmk::ScanParams kp{};
   kp.x = a->x;
@@ -361,6 +420,11 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_args_t* a, void* hip_stream) {
   kp.C = pl.C;
   kp.dtiles = int32_t(pl.dtiles);
   kp.exact_thr = exact_threshold(a->disc, a->in_dtype);
+  kp.dt_bias = a->delta_bias;
+  kp.dt_mode = dt_mode_of(a->delta_bias, a->delta_softplus);
+  kp.z = a->z;
+  kp.cs_in = a->conv_w ? a->conv_state_in : nullptr;
+  kp.cs_out = a->conv_w ? a->conv_state_out : nullptr;
   switch (a->dstate) {
     case 1: return dispatch_types<1>(a, kp, pl, s);
     case 2: return dispatch_types<2>(a, kp, pl, s);
@@ -387,6 +451,13 @@ ssm_status_t ssm_step(const ssm_step_args_t* a, void* hip_stream) {
   kp.Bt = a->batch;
   kp.D = a->dim;
   kp.exact_thr = exact_threshold(a->disc, a->in_dtype);
+  kp.dt_bias = a->delta_bias;
+  kp.dt_mode = dt_mode_of(a->delta_bias, a->delta_softplus);
+  kp.z = a->z;
+  kp.conv_k = a->conv_w ? a->conv_k : 0;
+  kp.conv_w = a->conv_w;
+  kp.conv_b = a->conv_w ? a->conv_b : nullptr;
+  kp.conv_state = a->conv_w ? a->conv_state : nullptr;
   switch (a->dstate) {
     case 1: return run_step_n<1>(a, kp, s);
     case 2: return run_step_n<2>(a, kp, s);

@@ -196,3 +196,32 @@ def decode_inputs(w: Workload, steps: Optional[int] = None, seed: Optional[int] 
     out["A"] = a_matrix(D, N)
     out["D"] = np.ones(D, dtype=np.float32)
     return out
+
+
+def fused_inputs(w: Workload, seed: Optional[int] = None, steps: Optional[int] = None) -> dict:
+    """Extra inputs of the fused steps around the scan, drawn after the
+    workload's own recipe:
+
+      delta_raw   (Bt, L, D)  pre-activation of the step size, 0.5 * N(0, 1),
+                              stored in the workload's dtype; with
+      delta_bias  (D,)        -4 + U(-0.5, 0.5) fp32, softplus(delta_raw +
+                              delta_bias) follows the Delta recipe above;
+      z           (Bt, L, D)  gate stream N(0, 1), workload dtype;
+      conv_state  (Bt, D, K-1) the inputs before token 0, N(0, 1) rounded to
+                              the workload's dtype (like x), fp32 storage.
+
+    With ``steps`` the per-token arrays get a leading (steps,) axis and no L
+    axis instead (decode inputs)."""
+    if seed is None:
+        seed = SEED_BASE + w.config_id + 500
+    rng = np.random.Generator(np.random.PCG64(seed))
+    Bt, L, D = w.batch, w.seqlen, w.dim
+    lead = (steps, Bt, D) if steps is not None else (Bt, L, D)
+    K = max(w.conv_k, 1)
+    out = {
+        "delta_raw": _store(np.float32(0.5) * _normal(rng, lead), w.in_dtype),
+        "delta_bias": (np.float32(-4.0) + rng.uniform(-0.5, 0.5, size=D)).astype(np.float32),
+        "z": _store(_normal(rng, lead), w.in_dtype),
+        "conv_state": _store(_normal(rng, (Bt, D, K - 1)), w.in_dtype),
+    }
+    return out

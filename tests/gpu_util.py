@@ -114,3 +114,76 @@ def channel_slice(inp, b, ds):
         out["conv_w"] = np.ascontiguousarray(inp["conv_w"][ds])
         out["conv_b"] = np.ascontiguousarray(inp["conv_b"][ds])
     return out
+
+
+def step_size_inputs(inp, ex, use):
+    """(delta given to the call, delta_bias or None, softplus flag) for the
+    fused steps in ``use``: with softplus the pre-activations of
+    ssm_inputs.fused_inputs and their bias; with a bias alone the workload's
+    positive Delta and a bias shifted into [0, 1], so Delta stays positive."""
+    if "softplus" in use:
+        return ex["delta_raw"], ex["delta_bias"], True
+    if "bias" in use:
+        return inp["delta"], (ex["delta_bias"] + np.float32(4.5)).astype(np.float32), False
+    return inp["delta"], None, False
+
+
+def fused_kwargs(inp, ex, use, dtype, to_dev=True):
+    """Keyword arguments of the fused steps selected by ``use`` (a set of
+    "softplus", "bias", "gate", "state") other than the conv window, from the
+    arrays of ssm_inputs.fused_inputs; device tensors when ``to_dev``."""
+    put = (lambda a, d="f32": dev(a, d)) if to_dev else (lambda a, d="f32": a)
+    _, bias, sp = step_size_inputs(inp, ex, use)
+    kw = {}
+    if bias is not None:
+        kw["delta_bias"] = put(bias)
+    if sp:
+        kw["delta_softplus"] = True
+    if "gate" in use:
+        kw["z"] = put(ex["z"], dtype)
+    return kw
+
+
+def gpu_scan_fused(inp, ex, use, in_dtype, out_dtype, zoh=False, chunk_len=0, h0=True):
+    """The library on numpy inputs with fused steps; the step-size input is
+    ex["delta_raw"] when softplus or bias is used.  Returns (y, h_last,
+    conv_state_out or None) as numpy."""
+    import torch
+    import selective_state_space_83_amd as ssm
+    t = {}
+    for k in ("x", "B", "C"):
+        t[k] = dev(inp[k], in_dtype)
+    t["delta"] = dev(step_size_inputs(inp, ex, use)[0], in_dtype)
+    for k in ("A", "D", "conv_w", "conv_b"):
+        t[k] = dev(inp.get(k))
+    t["h0"] = dev(inp.get("h0")) if h0 else None
+    kw = fused_kwargs(inp, ex, use, in_dtype)
+    cs_out = None
+    if inp.get("conv_w") is not None and "state" in use:
+        K = inp["conv_w"].shape[1]
+        kw["conv_state_in"] = dev(ex["conv_state"])
+        cs_out = torch.full((inp["x"].shape[0], inp["x"].shape[2], K - 1), float("nan"),
+                            device="cuda")
+        kw["conv_state_out"] = cs_out
+    y, hl = ssm.scan(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], h0=t["h0"],
+                     conv_w=t["conv_w"], conv_b=t["conv_b"], zoh=zoh,
+                     out_dtype=torch_dtype(out_dtype), chunk_len=chunk_len, **kw)
+    torch.cuda.synchronize()
+    return host(y), hl.cpu().numpy(), (cs_out.cpu().numpy() if cs_out is not None else None)
+
+
+def oracle_scan_fused(inp, ex, use, zoh=False, h0=True):
+    """The oracle on the same inputs as gpu_scan_fused."""
+    import oracle
+    kw = fused_kwargs(inp, ex, use, None, to_dev=False)
+    cs_out = None
+    if inp.get("conv_w") is not None and "state" in use:
+        K = inp["conv_w"].shape[1]
+        kw["conv_state_in"] = ex["conv_state"]
+        cs_out = np.zeros((inp["x"].shape[0], inp["x"].shape[2], K - 1))
+        kw["conv_state_out"] = cs_out
+    y, hl = oracle.default().scan(inp["x"], step_size_inputs(inp, ex, use)[0], inp["A"],
+                                  inp["B"], inp["C"], inp.get("D"),
+                                  h0=inp.get("h0") if h0 else None, conv_w=inp.get("conv_w"),
+                                  conv_b=inp.get("conv_b"), zoh=zoh, nthreads=threads(), **kw)
+    return y, hl, cs_out

@@ -77,7 +77,7 @@ def test_struct_layout_matches_header(tmp_path):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_abi_version() == 1
+    assert lib.ssm_abi_version() == 2
     for s in range(0, 8):
         assert lib.ssm_status_string(s)
     assert lib.ssm_status_string(99) == b"unknown status"
@@ -241,6 +241,97 @@ def test_empty_sequence_h_last_alias(lib):
     a.h0 = 0x100000000
     a.h_last = a.h0 + 64
     expect(lib, a, ssm.SSM_ERR_ALIAS)
+
+
+# ---------------------------------------------------------------------------
+# fused steps (softplus step size, gate, conv window)
+# ---------------------------------------------------------------------------
+
+def with_conv(a, k=4):
+    a.conv_w = 0x100000000 + 20 * GB
+    a.conv_k = k
+    return a
+
+
+def test_softplus_flag_and_reserved2(lib):
+    a = valid_scan_args()
+    a.delta_softplus = 2
+    expect(lib, a, ssm.SSM_ERR_UNSUPPORTED)
+    a = valid_scan_args()
+    a.reserved2 = 1
+    expect(lib, a, ssm.SSM_ERR_UNSUPPORTED)
+
+
+@pytest.mark.parametrize("field", ["conv_state_in", "conv_state_out"])
+def test_conv_state_needs_conv(lib, field):
+    a = valid_scan_args()
+    setattr(a, field, 0x100000000 + 21 * GB)
+    expect(lib, a, ssm.SSM_ERR_UNSUPPORTED)
+
+
+@pytest.mark.parametrize("inp", ["x", "delta", "conv_w", "conv_state_in", "z", "delta_bias"])
+def test_conv_state_out_aliases_input(lib, inp):
+    a = with_conv(valid_scan_args())
+    a.conv_state_in = 0x100000000 + 21 * GB
+    a.z = 0x100000000 + 22 * GB
+    a.delta_bias = 0x100000000 + 23 * GB
+    a.conv_state_out = getattr(a, inp)
+    expect(lib, a, ssm.SSM_ERR_ALIAS)
+
+
+@pytest.mark.parametrize("out", ["y", "h_last", "workspace"])
+def test_conv_state_out_aliases_output(lib, out):
+    a = with_conv(valid_scan_args(batch=1, L=4096, D=64))
+    a.conv_state_out = getattr(a, out) + 4
+    expect(lib, a, ssm.SSM_ERR_ALIAS)
+
+
+@pytest.mark.parametrize("inp", ["z", "delta_bias"])
+def test_y_aliases_fused_input(lib, inp):
+    a = valid_scan_args()
+    a.z = 0x100000000 + 22 * GB
+    a.delta_bias = 0x100000000 + 23 * GB
+    a.y = getattr(a, inp)
+    expect(lib, a, ssm.SSM_ERR_ALIAS)
+
+
+def test_fused_misaligned(lib):
+    a = valid_scan_args()
+    a.z = 0x100000000 + 22 * GB + 2
+    expect(lib, a, ssm.SSM_ERR_UNSUPPORTED)
+    a = with_conv(valid_scan_args())
+    a.conv_state_out = 0x100000000 + 21 * GB + 2
+    expect(lib, a, ssm.SSM_ERR_UNSUPPORTED)
+
+
+def test_empty_sequence_conv_state_alias(lib):
+    a = ssm.ScanArgs()
+    a.batch, a.seqlen, a.dim, a.dstate = 2, 0, 8, 16
+    with_conv(a, 3)
+    a.conv_state_in = 0x100000000
+    a.conv_state_out = a.conv_state_in + 8
+    expect(lib, a, ssm.SSM_ERR_ALIAS)
+
+
+def test_step_fused_errors(lib):
+    s = valid_step_args()
+    s.delta_softplus = 7
+    assert step_call(lib, s) == ssm.SSM_ERR_UNSUPPORTED
+    s = valid_step_args()
+    s.conv_w, s.conv_k = 0x100000000 + 20 * GB, 5
+    assert step_call(lib, s) == ssm.SSM_ERR_UNSUPPORTED
+    s = valid_step_args()
+    s.conv_w, s.conv_k = 0x100000000 + 20 * GB, 4      # window of 3 needs a state
+    assert step_call(lib, s) == ssm.SSM_ERR_NULL
+    s.conv_state = s.h + 64
+    assert step_call(lib, s) == ssm.SSM_ERR_ALIAS
+    s.conv_state = s.x
+    assert step_call(lib, s) == ssm.SSM_ERR_ALIAS
+    s.conv_state = 0x100000000 + 21 * GB + 2
+    assert step_call(lib, s) == ssm.SSM_ERR_UNSUPPORTED
+    s = valid_step_args()
+    s.z = s.y
+    assert step_call(lib, s) == ssm.SSM_ERR_ALIAS
 
 
 # ---------------------------------------------------------------------------
