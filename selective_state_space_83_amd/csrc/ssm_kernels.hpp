@@ -411,7 +411,9 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
                                            uint32_t lo, int64_t t0, int32_t steps, float (&h)[N],
                                            float* dsum_out, float* cs_save) {
   static_assert(OUT || !GATE, "the gate applies to the output pass");
-  constexpr int kU = OUT ? kUnrollOut : kUnrollSum;
+  // (the conv prologue's extra registers would push an 8-step summary block
+  // past 128 VGPRs, so conv summaries prefetch 6 steps ahead)
+  constexpr int kU = OUT ? kUnrollOut : (CONV ? 6 : kUnrollSum);
   const int64_t d = dbase + lo;
   ChanConst<N, DISC> cc;
   load_chan<N, DISC>(cc, p.A + d * N, p.exact_thr);
@@ -571,8 +573,10 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
 
 // Pass 1 (chunked plans): for chunks 0..C-2, the state each chunk reaches from
 // a zero state, and its sum of Delta.
+// (at most 128 VGPRs, i.e. at least four waves per SIMD, for every variant)
 template <int N, typename InT, int DISC, bool CONV>
-__global__ void __launch_bounds__(kWave) k_chunk_summary(const ScanParams p) {
+__global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(4)))
+k_chunk_summary(const ScanParams p) {
   const int wg = xcd_remap(blockIdx.x, p.nwg);
   const Tile tl = tile_of(wg, p.dtiles, p.C - 1);
   const int64_t dbase = tl.dtile * kWave;
@@ -637,7 +641,8 @@ __global__ void __launch_bounds__(kWave) k_carry_combine(const ScanParams p) {
 // Pass 3 (or the only pass): scan each chunk from its carry-in, write y, and
 // h_last from the final chunk.
 template <int N, typename InT, typename OutT, int DISC, bool CONV, bool GATE>
-__global__ void __launch_bounds__(kWave) k_scan_out(const ScanParams p) {
+__global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(4)))
+k_scan_out(const ScanParams p) {
   const int wg = xcd_remap(blockIdx.x, p.nwg);
   const Tile tl = tile_of(wg, p.dtiles, p.C);
   const int64_t dbase = tl.dtile * kWave;
