@@ -22,6 +22,11 @@ kernel on the launch stream.  Two roofs are evaluated:
        Delta*B (v_mul, v_exp at half rate = 2, v_mul, v_fma, v_fma) or 8 for
        ZOH, plus 2 slots per (b, t, d) (Delta*u and the skip term).
 The reported bound is the roof with the higher utilisation.
+
+--fused runs the same workload with every fused step on: the step size from
+its pre-activation (softplus(delta + bias[d])), the gate y * silu(z) and, with
+a conv, the conv window read from and handed back to a state buffer; the
+decode workload then also runs a 4-tap conv over its rolling window.
 """
 from __future__ import annotations
 
@@ -40,6 +45,7 @@ import numpy as np  # noqa: E402
 
 METRIC = "scan elems (B·L·D·N)/s and achieved HBM GB/s vs MI355X peak, 1 GPU"
 HBM_PEAK_GBS = 8000.0
+FUSED_DECODE_CONV_K = 4                    # conv taps of the fused decode run
 SLOT_PEAK = 256 * 4 * 16 * 2.4e9          # VALU lane-slots per second
 KERNEL_SRC = os.path.join(ROOT, "selective_state_space_83_amd", "csrc", "ssm_kernels.hpp")
 
@@ -88,7 +94,7 @@ class HipEvents:
 # algorithmic work
 # ---------------------------------------------------------------------------
 
-def algorithmic_bytes(w, h0=False, h_last=False) -> int:
+def algorithmic_bytes(w, h0=False, h_last=False, fused=False) -> int:
     s_in = 2 if w.in_dtype == "bf16" else 4
     s_out = 2 if w.out_dtype == "bf16" else 4
     Bt, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
@@ -96,14 +102,27 @@ def algorithmic_bytes(w, h0=False, h_last=False) -> int:
     if w.conv_k:
         n += 4 * D * w.conv_k + 4 * D
     n += 4 * Bt * D * N * (int(h0) + int(h_last))
+    if fused:
+        n += Bt * L * D * s_in + 4 * D                 # z, delta_bias
+        if w.conv_k:
+            n += 2 * 4 * Bt * D * (w.conv_k - 1)        # conv window in and out
     return n
 
 
-def algorithmic_slots(w) -> float:
+# VALU lane-slots per (b, t, d) of the fused steps: softplus (bias add, scale,
+# exp (2), 1 + e, compare + select, log (2), 2 muls, sub, rcp (2)) and the
+# gate (scale, exp (2), add, rcp (2), 2 muls)
+SLOTS_SOFTPLUS = 15.0
+SLOTS_GATE = 8.0
+
+
+def algorithmic_slots(w, fused=False) -> float:
     per_elem = 8.0 if w.zoh else 6.0
     per_btd = 2.0
     if w.conv_k:
         per_btd += 4 + 2 + 2 + 2   # 4 taps, exp (2), rcp (2), add + mul of SiLU
+    if fused:
+        per_btd += SLOTS_SOFTPLUS + SLOTS_GATE
     Bt, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
     return Bt * L * D * (N * per_elem + per_btd)
 
@@ -134,7 +153,7 @@ def to_dev(a, dtype, torch):
     return t.cuda()
 
 
-def bench_scan(w, steps, warmup, torch, ssm, chunk_len=0):
+def bench_scan(w, steps, warmup, torch, ssm, chunk_len=0, fused=False):
     import ssm_inputs as SI
     inp = SI.scan_inputs(w)
     t = {k: to_dev(inp[k], w.in_dtype, torch) for k in ("x", "delta", "B", "C")}
@@ -142,11 +161,20 @@ def bench_scan(w, steps, warmup, torch, ssm, chunk_len=0):
         t[k] = to_dev(inp[k], "f32", torch)
     odt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
     y = torch.empty(t["x"].shape, dtype=odt, device="cuda")
+    kw = {}
+    if fused:
+        ex = SI.fused_inputs(w)
+        t["delta"] = to_dev(ex["delta_raw"], w.in_dtype, torch)
+        kw = dict(delta_bias=to_dev(ex["delta_bias"], "f32", torch), delta_softplus=True,
+                  z=to_dev(ex["z"], w.in_dtype, torch))
+        if w.conv_k:
+            kw["conv_state_in"] = to_dev(ex["conv_state"], "f32", torch)
+            kw["conv_state_out"] = torch.empty_like(kw["conv_state_in"])
     # arguments are checked and marshalled once, so the timed loop measures
     # the library's launches rather than Python argument handling
     prep, y, _ = ssm.prepare_scan(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"],
                                   conv_w=t["conv_w"], conv_b=t["conv_b"], zoh=w.zoh, y=y,
-                                  chunk_len=chunk_len)
+                                  chunk_len=chunk_len, **kw)
     ws_bytes = ssm.workspace_size(prep.args)
     chunk = ssm.plan_chunk_len(prep.args)
     hip = HipEvents()
@@ -190,7 +218,7 @@ def bench_scan(w, steps, warmup, torch, ssm, chunk_len=0):
                 chunk_len=chunk, chunks=-(-w.seqlen // chunk), workspace=ws_bytes)
 
 
-def bench_decode(w, steps, warmup, torch, ssm):
+def bench_decode(w, steps, warmup, torch, ssm, fused=False):
     """One step = `w.steps` consecutive ssm_step calls (a 512-token decode)."""
     import ssm_inputs as SI
     n = w.steps
@@ -199,8 +227,19 @@ def bench_decode(w, steps, warmup, torch, ssm):
     A, Dv = to_dev(inp["A"], "f32", torch), to_dev(inp["D"], "f32", torch)
     xs, ds_, Bs, Cs = (to_dev(inp[k], w.in_dtype, torch) for k in ("x", "delta", "B", "C"))
     y = torch.empty((w.batch, w.dim), dtype=torch.bfloat16, device="cuda")
+    per_tok = [{} for _ in range(n)]
+    if fused:
+        ex = SI.fused_inputs(w.with_(conv_k=FUSED_DECODE_CONV_K), steps=n)
+        ds_ = to_dev(ex["delta_raw"], w.in_dtype, torch)
+        zs = to_dev(ex["z"], w.in_dtype, torch)
+        common = dict(delta_bias=to_dev(ex["delta_bias"], "f32", torch), delta_softplus=True,
+                      conv_w=to_dev(ex["conv_w"], "f32", torch),
+                      conv_b=to_dev(ex["conv_b"], "f32", torch),
+                      conv_state=to_dev(ex["conv_state"], "f32", torch))
+        per_tok = [dict(common, z=zs[s]) for s in range(n)]
     # arguments marshalled once per token; the timed loop only launches
-    calls = [ssm.prepare_step(h, xs[s], ds_[s], A, Bs[s], Cs[s], Dv, y=y)[0] for s in range(n)]
+    calls = [ssm.prepare_step(h, xs[s], ds_[s], A, Bs[s], Cs[s], Dv, y=y, **per_tok[s])[0]
+             for s in range(n)]
     stream = torch.cuda.current_stream()
 
     def run():
@@ -262,6 +301,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused", action="store_true",
+                    help="run with the fused steps on (softplus step size, gate, conv window)")
     ap.add_argument("--chunk-len", type=int, default=0,
                     help="force the scan's chunk length (0 = the library's plan)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -292,13 +333,18 @@ def main():
     log("bench: workload %s, %d warmup + %d timed steps" % (w, args.warmup, args.steps))
 
     if w.steps:
-        r = bench_decode(w, args.steps, args.warmup, torch, ssm)
+        r = bench_decode(w, args.steps, args.warmup, torch, ssm, fused=args.fused)
         ms = r["total_ms"] / args.steps
         elems = w.elems
         # per token: h read + written (fp32), x, Delta, y (bf16), B, C rows
         s_in = 2 if w.in_dtype == "bf16" else 4
         per_launch = (2 * 4 * w.batch * w.dim * w.dstate + w.batch * w.dim * 3 * s_in
                       + 2 * w.batch * w.dstate * s_in + 4 * w.dim * (w.dstate + 1))
+        if args.fused:
+            # z, delta_bias, conv weights and bias, the fp32 window read and written
+            K = FUSED_DECODE_CONV_K
+            per_launch += (w.batch * w.dim * s_in + 4 * w.dim * (2 + K)
+                           + 2 * 4 * w.batch * w.dim * (K - 1))
         bytes_ = w.steps * per_launch
         ach = per_launch / (r["launch_us"] * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -310,23 +356,24 @@ def main():
                "dtype": "f32", "data": "synthetic",
                "config": {"workload": "decode", "batch": w.batch, "dim": w.dim,
                           "dstate": w.dstate, "tokens_per_step": w.steps,
-                          "in_dtype": w.in_dtype, "state": "f32"},
+                          "in_dtype": w.in_dtype, "state": "f32",
+                          "fused": "softplus+gate+conv4" if args.fused else None},
                "hbm_gbps": bytes_ / (ms * 1e-3) / 1e9,
                "roofline": roof, "cpu_baseline": None}
         print(json.dumps(out), flush=True)
         return
 
-    r = bench_scan(w, args.steps, args.warmup, torch, ssm, args.chunk_len)
+    r = bench_scan(w, args.steps, args.warmup, torch, ssm, args.chunk_len, fused=args.fused)
     ms = r["total_ms"] / args.steps
     elems = w.elems
     out_us = float(np.mean(r["out_ms"])) * 1e3
-    abytes = algorithmic_bytes(w)
-    slots = algorithmic_slots(w)
+    abytes = algorithmic_bytes(w, fused=args.fused)
+    slots = algorithmic_slots(w, fused=args.fused)
     hbm_ach = abytes / (out_us * 1e-6) / 1e9
     alu_ach = slots / (out_us * 1e-6) / 1e12
     hbm_frac = hbm_ach / HBM_PEAK_GBS
     alu_frac = alu_ach / (SLOT_PEAK / 1e12)
-    traffic = traffic_record(w.name)
+    traffic = None if args.fused else traffic_record(w.name)
     if alu_frac > hbm_frac:
         roof = {"bound": "alu", "achieved": alu_ach, "peak": SLOT_PEAK / 1e12,
                 "unit": "T lane-slot/s", "frac": alu_frac, "traffic": traffic}
@@ -339,7 +386,7 @@ def main():
     roof["alu_view"] = {"achieved_tslots": alu_ach, "frac": alu_frac}
     whole_gbps = abytes / (ms * 1e-3) / 1e9
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.fused:
         log("bench: timing the oracle on the host")
         cpu = cpu_baseline(w, r["inp"])
     dtype = "f32"   # arithmetic and state are fp32 for every storage dtype
@@ -350,7 +397,9 @@ def main():
            "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                       "dstate": w.dstate, "in_dtype": w.in_dtype, "out_dtype": w.out_dtype,
                       "disc": "zoh" if w.zoh else "delta_b", "conv_k": w.conv_k,
-                      "chunk_len": r["chunk_len"], "chunks": r["chunks"]},
+                      "chunk_len": r["chunk_len"], "chunks": r["chunks"],
+                      "fused": ("softplus+gate" + ("+conv_state" if w.conv_k else ""))
+                      if args.fused else None},
            "hbm_gbps": whole_gbps, "hbm_frac": whole_gbps / HBM_PEAK_GBS,
            "flushed_ms_per_step": float(np.median(r["flushed_ms"])),
            "roofline": roof, "cpu_baseline": cpu}

@@ -174,7 +174,8 @@ __device__ __forceinline__ float silu(float z) {
 __device__ __forceinline__ float softplus(float v) {
   const float e = exp2_fast(-fabsf(v) * kLog2e);
   const float w = 1.0f + e;
-  const float l = (w == 1.0f) ? e : (__builtin_amdgcn_logf(w) * kLn2) * (e / (w - 1.0f));
+  const float l =
+      (w == 1.0f) ? e : (__builtin_amdgcn_logf(w) * kLn2) * (e * __builtin_amdgcn_rcpf(w - 1.0f));
   return fmaxf(v, 0.0f) + l;
 }
 
@@ -782,19 +783,22 @@ __global__ void __launch_bounds__(kWave) k_step(const StepParams p) {
     float dv = ld(static_cast<const InT*>(p.delta) + b * p.D + d);
     if (dtm != kDtRaw) dv = dt_transform(dv, dtb, dtm);
     if (K > 0) {
-      // window x[-SW .. -1] (oldest first), then the new input
+      // window x[-SW .. -1] (oldest first) as x[-3], x[-2], x[-1] (zero where
+      // the window is shorter), then the new input; three independent loads
       float* win = p.conv_state + (b * p.D + d) * SW;
-      float xm[3] = {0.f, 0.f, 0.f};
-      for (int k = 0; k < SW; ++k) xm[3 - SW + k] = win[k];
+      const float xm3 = SW >= 3 ? win[SW - 3] : 0.0f;
+      const float xm2 = SW >= 2 ? win[SW - 2] : 0.0f;
+      const float xm1 = SW >= 1 ? win[SW - 1] : 0.0f;
       float zc = fmaf(cw[3], u, cb);
-      zc = fmaf(cw[2], xm[2], zc);
-      zc = fmaf(cw[1], xm[1], zc);
-      zc = fmaf(cw[0], xm[0], zc);
+      zc = fmaf(cw[2], xm1, zc);
+      zc = fmaf(cw[1], xm2, zc);
+      zc = fmaf(cw[0], xm3, zc);
       // the window moves on by one input (written by one lane per channel,
       // after every lane of the wave has read it in the loads above)
-      if (j == 0 && SW > 0) {
-        for (int k = 0; k + 1 < SW; ++k) win[k] = xm[3 - SW + k + 1];
-        win[SW - 1] = u;
+      if (j == 0) {
+        if (SW >= 3) win[SW - 3] = xm2;
+        if (SW >= 2) win[SW - 2] = xm1;
+        if (SW >= 1) win[SW - 1] = u;
       }
       u = silu(zc);
     }

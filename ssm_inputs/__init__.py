@@ -208,7 +208,8 @@ def fused_inputs(w: Workload, seed: Optional[int] = None, steps: Optional[int] =
                               delta_bias) follows the Delta recipe above;
       z           (Bt, L, D)  gate stream N(0, 1), workload dtype;
       conv_state  (Bt, D, K-1) the inputs before token 0, N(0, 1) rounded to
-                              the workload's dtype (like x), fp32 storage.
+                              the workload's dtype (like x), fp32 storage;
+      conv_w, conv_b          (with a conv) weights 0.5 * N(0, 1) and zero bias.
 
     With ``steps`` the per-token arrays get a leading (steps,) axis and no L
     axis instead (decode inputs)."""
@@ -224,4 +225,9 @@ def fused_inputs(w: Workload, seed: Optional[int] = None, steps: Optional[int] =
         "z": _store(_normal(rng, lead), w.in_dtype),
         "conv_state": _store(_normal(rng, (Bt, D, K - 1)), w.in_dtype),
     }
+    if w.conv_k:
+        # the conv weights of the workload recipe, for callers (decode) whose
+        # scan inputs carry none
+        out["conv_w"] = (np.float32(0.5) * _normal(rng, (D, w.conv_k))).astype(np.float32)
+        out["conv_b"] = np.zeros(D, dtype=np.float32)
     return out
