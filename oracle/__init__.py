@@ -47,6 +47,9 @@ class Oracle:
         lib.ssm_ref_step_f64.argtypes = [i64, i64, i64, dp, dp, dp, dp, ci, dp, dp, dp, dp,
                                          dp, dp, dp, i64, dp, ci, dp, ci]
         lib.ssm_ref_step_f64.restype = ctypes.c_int
+        lib.ssm_ref_scan_bwd_f64.argtypes = [i64, i64, i64, i64, dp, dp, dp, dp, dp, dp, dp,
+                                             dp, dp, ci, dp, dp, dp, dp, dp, dp, dp, ci]
+        lib.ssm_ref_scan_bwd_f64.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -137,6 +140,36 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
         return (y, h) if conv_w is None else (y, h, cs)
+
+    def scan_bwd(self, x, delta, A, B, C, dy, D=None, h0=None, dh_last=None, zoh=False,
+                 nthreads=0):
+        """Gradients of sum(dy * y) + sum(dh_last * h_last) for the scan
+        without conv prologue.  Returns a dict of float64 arrays: dx, ddelta
+        (batch, L, dim), dA (dim, N), dB, dC (batch, L, N), dD (dim,), dh0
+        (batch, dim, N)."""
+        x, delta, A, B, C, dy = map(self._f64, (x, delta, A, B, C, dy))
+        D, h0, dh_last = map(self._f64, (D, h0, dh_last))
+        batch, L, dim = x.shape
+        N = A.shape[1]
+        assert delta.shape == x.shape and dy.shape == x.shape and A.shape == (dim, N)
+        assert B.shape == (batch, L, N) and C.shape == (batch, L, N)
+        for v, shp in ((D, (dim,)), (h0, (batch, dim, N)), (dh_last, (batch, dim, N))):
+            if v is not None:
+                assert v.shape == shp, (v.shape, shp)
+        g = {"dx": np.zeros(x.shape), "ddelta": np.zeros(x.shape), "dA": np.zeros((dim, N)),
+             "dB": np.zeros(B.shape), "dC": np.zeros(C.shape), "dD": np.zeros(dim),
+             "dh0": np.zeros((batch, dim, N))}
+        rc = self.lib.ssm_ref_scan_bwd_f64(batch, L, dim, N, self._ptr(x), self._ptr(delta),
+                                           self._ptr(A), self._ptr(B), self._ptr(C),
+                                           self._ptr(D), self._ptr(h0), self._ptr(dy),
+                                           self._ptr(dh_last), int(bool(zoh)),
+                                           self._ptr(g["dx"]), self._ptr(g["ddelta"]),
+                                           self._ptr(g["dA"]), self._ptr(g["dB"]),
+                                           self._ptr(g["dC"]), self._ptr(g["dD"]),
+                                           self._ptr(g["dh0"]), int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return g
 
 
 _default = None

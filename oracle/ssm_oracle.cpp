@@ -47,6 +47,14 @@
 //     as one call (the recurrent, constant-cost-per-token inference mode:
 //     53ai.com explainer, section "一、Motivation").
 //
+// The backward pass (O3) is the reverse-mode derivative of the same
+// sequential recurrence, written out with the chain rule and evaluated in
+// fp64 from the last token to the first; the forward states it needs are
+// kept from a plain forward sweep.  (The pages name training as the use of
+// the parallel scan -- 53ai.com explainer, section "3.6 Empirical
+// Evaluation" and VMamba note, section "硬件感知的设计" -- but print no
+// gradient formula; the derivative of the defined function is the reading.)
+//
 // Readings where the pages are silent (listed in the design notes too):
 //   - the initial state h0 precedes token 0, so y_0 already contains x_0;
 //   - Abar at step t uses Delta_t, the same step as x_t;
@@ -164,6 +172,92 @@ int pick_threads(int requested, int64_t work_items) {
   return n;
 }
 
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+
+struct BwdProblem {
+  int64_t batch, seqlen, dim, dstate;
+  const double *x, *delta, *A, *Bm, *Cm, *Dskip, *h0, *dy, *dh_last;
+  int zoh;
+  double *dx, *ddelta, *dB, *dC, *dh0;   // dB, dC: rows of the batch rows a worker owns
+};
+
+// d(input factor)/d(Delta) and d(input factor)/dA for the factor f used in
+// Bbar = f * B: Delta*B has f = Delta (derivatives 1 and 0); ZOH has
+// f = (exp(Delta A) - 1) / A, so df/dDelta = exp(Delta A) and
+// df/dA = (Delta exp(Delta A) - f) / A, whose A -> 0 limit is Delta^2 / 2.
+void factor_derivs(double dt, double a_cont, int zoh, double* df_dt, double* df_da) {
+  if (!zoh) {
+    *df_dt = 1.0;
+    *df_da = 0.0;
+    return;
+  }
+  if (a_cont == 0.0) {
+    *df_dt = 1.0;
+    *df_da = 0.5 * dt * dt;
+    return;
+  }
+  const double e = std::exp(dt * a_cont);
+  *df_dt = e;
+  *df_da = (dt * e - std::expm1(dt * a_cont) / a_cont) / a_cont;
+}
+
+// Gradients for batch row b (all channels), accumulating dA (D, N) and
+// dD (D) into the worker's own buffers.
+void bwd_batch_row(const BwdProblem& p, int64_t b, std::vector<double>& dA,
+                   std::vector<double>& dD) {
+  const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
+  std::vector<double> H((L + 1) * N);   // H[(t + 1) * N + n] = h_t[n], row 0 = h_{-1}
+  std::vector<double> g(N);
+  for (int64_t d = 0; d < D; ++d) {
+    // forward sweep keeping every state
+    for (int64_t n = 0; n < N; ++n) H[n] = p.h0 ? p.h0[(b * D + d) * N + n] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+      const double u = p.x[(b * L + t) * D + d];
+      const double dt = p.delta[(b * L + t) * D + d];
+      for (int64_t n = 0; n < N; ++n) {
+        const double a_cont = p.A[d * N + n];
+        H[(t + 1) * N + n] = std::exp(dt * a_cont) * H[t * N + n] +
+                             input_factor(dt, a_cont, p.zoh) * p.Bm[(b * L + t) * N + n] * u;
+      }
+    }
+    // reverse sweep: g[n] is dLoss/dh_t[n] once token t's output term is added
+    for (int64_t n = 0; n < N; ++n) g[n] = p.dh_last ? p.dh_last[(b * D + d) * N + n] : 0.0;
+    const double dskip = p.Dskip ? p.Dskip[d] : 0.0;
+    for (int64_t t = L - 1; t >= 0; --t) {
+      const double u = p.x[(b * L + t) * D + d];
+      const double dt = p.delta[(b * L + t) * D + d];
+      const double gy = p.dy[(b * L + t) * D + d];
+      double du = dskip * gy, ddt = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        const double a_cont = p.A[d * N + n];
+        const double Bn = p.Bm[(b * L + t) * N + n];
+        const double Cn = p.Cm[(b * L + t) * N + n];
+        const double h_prev = H[t * N + n];
+        const double h_now = H[(t + 1) * N + n];
+        const double G = g[n] + Cn * gy;                 // y_t = sum C h_t + ...
+        const double abar = std::exp(dt * a_cont);
+        const double f = input_factor(dt, a_cont, p.zoh);
+        double df_dt, df_da;
+        factor_derivs(dt, a_cont, p.zoh, &df_dt, &df_da);
+        p.dC[(b * L + t) * N + n] += gy * h_now;
+        p.dB[(b * L + t) * N + n] += G * f * u;
+        du += G * f * Bn;
+        // h_t = exp(dt A) h_{t-1} + f(dt, A) B u
+        ddt += G * (a_cont * abar * h_prev + df_dt * Bn * u);
+        dA[d * N + n] += G * (dt * abar * h_prev + df_da * Bn * u);
+        g[n] = abar * G;                                  // into h_{t-1}
+      }
+      p.dx[(b * L + t) * D + d] = du;
+      p.ddelta[(b * L + t) * D + d] = ddt;
+      dD[d] += gy * u;
+    }
+    if (p.dh0)
+      for (int64_t n = 0; n < N; ++n) p.dh0[(b * D + d) * N + n] = g[n];
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -225,6 +319,52 @@ int ssm_ref_step_f64(int64_t batch, int64_t dim, int64_t dstate, double* h,
   return ssm_ref_scan_f64(batch, 1, dim, dstate, x, delta, delta_bias, delta_softplus, A, Bm,
                           Cm, Dskip, z, h, conv_w, conv_b, conv_k, conv_state, zoh, y, h,
                           conv_state, nthreads);
+}
+
+// O3: gradients of the scalar loss sum(dy * y) + sum(dh_last * h_last) of
+// O1 without conv prologue: dx, ddelta (batch, L, D), dA (D, N), dB, dC
+// (batch, L, N), dD (D) and dh0 (batch, D, N) when their pointers are
+// given.  dy is (batch, L, D); dh_last (batch, D, N) or NULL.  Outputs are
+// overwritten.  Workers split the batch rows; dA and dD are summed over the
+// workers in worker order.  Returns 0, or -1 on a bad argument.
+int ssm_ref_scan_bwd_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                         const double* x, const double* delta, const double* A,
+                         const double* Bm, const double* Cm, const double* Dskip,
+                         const double* h0, const double* dy, const double* dh_last, int zoh,
+                         double* dx, double* ddelta, double* dA, double* dB, double* dC,
+                         double* dD, double* dh0, int nthreads) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1) return -1;
+  if (!A || !dA) return -1;
+  if (batch * seqlen * dim > 0 && (!x || !delta || !Bm || !Cm || !dy || !dx || !ddelta ||
+                                   !dB || !dC))
+    return -1;
+  const int64_t D = dim, N = dstate;
+  for (int64_t i = 0; i < D * N; ++i) dA[i] = 0.0;
+  if (dD)
+    for (int64_t i = 0; i < D; ++i) dD[i] = 0.0;
+  if (batch * seqlen > 0) {
+    for (int64_t i = 0; i < batch * seqlen * N; ++i) dB[i] = dC[i] = 0.0;
+  }
+  if (batch * dim == 0) return 0;
+  BwdProblem p{batch, seqlen, dim, dstate, x, delta, A, Bm, Cm, Dskip, h0, dy, dh_last, zoh,
+               dx, ddelta, dB, dC, dh0};
+  const int nt = pick_threads(nthreads, batch);
+  std::vector<std::vector<double>> dA_w(nt, std::vector<double>(D * N, 0.0));
+  std::vector<std::vector<double>> dD_w(nt, std::vector<double>(D, 0.0));
+  auto work = [&](int w) {
+    for (int64_t b = batch * w / nt; b < batch * (w + 1) / nt; ++b)
+      bwd_batch_row(p, b, dA_w[w], dD_w[w]);
+  };
+  std::vector<std::thread> pool;
+  for (int w = 1; w < nt; ++w) pool.emplace_back(work, w);
+  work(0);
+  for (auto& th : pool) th.join();
+  for (int w = 0; w < nt; ++w) {
+    for (int64_t i = 0; i < D * N; ++i) dA[i] += dA_w[w][i];
+    if (dD)
+      for (int64_t i = 0; i < D; ++i) dD[i] += dD_w[w][i];
+  }
+  return 0;
 }
 
 }  // extern "C"

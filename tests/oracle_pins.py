@@ -646,6 +646,94 @@ def pin_decode_conv_equals_scan(orc):
         _rel_close(cs, cs_scan, 0.0, "decode+conv window")
 
 
+# --------------------------------------------------------------------------
+# P13: backward pass = derivative of the forward pass (the pages give no
+#      gradient formula; the derivative of the defined function is fixed by
+#      the mathematics).  Checked against central finite differences of the
+#      oracle's forward scan, and against homogeneity identities at sizes
+#      where differencing every input would be slow.
+# --------------------------------------------------------------------------
+
+_BWD_INPUTS = ("x", "delta", "A", "B", "C", "D", "h0")
+_BWD_GRAD = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD",
+             "h0": "dh0"}
+
+
+def _bwd_problem(rng, Bt, L, D, N):
+    x, delta, A, B, C, Dsk = _random_problem(rng, Bt, L, D, N)
+    return dict(x=x, delta=delta, A=A, B=B, C=C, D=Dsk, h0=rng.standard_normal((Bt, D, N)))
+
+
+def _loss(orc, v, dy, dhl, zoh):
+    y, hl = orc.scan(v["x"], v["delta"], v["A"], v["B"], v["C"], D=v["D"], h0=v["h0"], zoh=zoh)
+    return float((dy * y).sum() + (dhl * hl).sum())
+
+
+def pin_bwd_finite_differences(orc):
+    """Every gradient (dx, dDelta, dA, dB, dC, dD, dh0) equals the central
+    difference (eps = 1e-6) of the loss sum(dy y) + sum(dh_last h_last),
+    both discretizations, including an A entry exactly 0 for ZOH."""
+    rng = _rng(130)
+    Bt, L, D, N = 2, 6, 2, 3
+    for zoh in (False, True):
+        v = _bwd_problem(rng, Bt, L, D, N)
+        if zoh:
+            v["A"][1, 2] = 0.0
+        dy = rng.standard_normal((Bt, L, D))
+        dhl = rng.standard_normal((Bt, D, N))
+        g = orc.scan_bwd(v["x"], v["delta"], v["A"], v["B"], v["C"], dy, D=v["D"], h0=v["h0"],
+                         dh_last=dhl, zoh=zoh)
+        eps = 1e-6
+        for name in _BWD_INPUTS:
+            arr = v[name]
+            num = np.zeros_like(arr)
+            for i in np.ndindex(arr.shape):
+                w = dict(v)
+                ap = arr.copy()
+                ap[i] += eps
+                w[name] = ap
+                lp = _loss(orc, w, dy, dhl, zoh)
+                am = arr.copy()
+                am[i] -= eps
+                w[name] = am
+                lm = _loss(orc, w, dy, dhl, zoh)
+                num[i] = (lp - lm) / (2 * eps)
+            got = g[_BWD_GRAD[name]]
+            scale = max(1.0, float(np.abs(num).max()))
+            err = float(np.abs(got - num).max())
+            assert err <= 1e-7 * scale, ("d" + name, zoh, err, scale)
+
+
+def pin_bwd_homogeneity(orc):
+    """Degree-one homogeneity (Euler): the loss is linear in (x, h0) jointly,
+    in C apart from the skip and h_last terms, and -- with h0 = 0 -- in B
+    apart from the skip term, so L = sum(dx x) + sum(dh0 h0),
+    sum(dC C) = L - sum(dy D u) - sum(dh_last h_last) and
+    sum(dB B) = L - sum(dy D u).  Also dD = sum over b, t of dy * x."""
+    rng = _rng(131)
+    Bt, L, D, N = 2, 150, 3, 4
+    for zoh in (False, True):
+        v = _bwd_problem(rng, Bt, L, D, N)
+        dy = rng.standard_normal((Bt, L, D))
+        dhl = rng.standard_normal((Bt, D, N))
+        g = orc.scan_bwd(v["x"], v["delta"], v["A"], v["B"], v["C"], dy, D=v["D"], h0=v["h0"],
+                         dh_last=dhl, zoh=zoh)
+        loss = _loss(orc, v, dy, dhl, zoh)
+        skip = float((dy * v["D"] * v["x"]).sum())
+        _, hl = orc.scan(v["x"], v["delta"], v["A"], v["B"], v["C"], D=v["D"], h0=v["h0"],
+                         zoh=zoh)
+        last = float((dhl * hl).sum())          # h_last does not depend on C
+        tol = 1e-11 * max(1.0, abs(loss))
+        assert abs((g["dx"] * v["x"]).sum() + (g["dh0"] * v["h0"]).sum() - loss) <= tol
+        assert abs((g["dC"] * v["C"]).sum() - (loss - skip - last)) <= tol
+        _rel_close(g["dD"], (dy * v["x"]).sum(axis=(0, 1)), 1e-13, "dD")
+        w = dict(v, h0=np.zeros_like(v["h0"]))
+        g0 = orc.scan_bwd(w["x"], w["delta"], w["A"], w["B"], w["C"], dy, D=w["D"],
+                          h0=w["h0"], dh_last=dhl, zoh=zoh)
+        loss0 = _loss(orc, w, dy, dhl, zoh)
+        assert abs((g0["dB"] * w["B"]).sum() - (loss0 - skip)) <= 1e-11 * max(1.0, abs(loss0))
+
+
 ALL_PINS = [
     pin_hand_expansion_lti, pin_hand_expansion_selective, pin_lti_kernel,
     pin_lti_steady_state, pin_brute_force, pin_split_invariance,
@@ -653,5 +741,5 @@ ALL_PINS = [
     pin_special_cases, pin_decode_equals_scan, pin_conv_identity_tap,
     pin_conv_numpy, pin_conv_scan_brute, pin_softplus_delta, pin_softplus_values, pin_gate,
     pin_conv_state_window, pin_conv_state_prefix, pin_conv_split_invariance,
-    pin_decode_conv_equals_scan,
+    pin_decode_conv_equals_scan, pin_bwd_finite_differences, pin_bwd_homogeneity,
 ]

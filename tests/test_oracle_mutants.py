@@ -14,7 +14,8 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "ssm_oracle.cpp")
 # (name, text in the oracle, replacement)
 MUTANTS = [
     ("input_sign", "h[n] = abar * h[n] + bbar * u;", "h[n] = abar * h[n] - bbar * u;"),
-    ("decay_sign", "std::exp(dt * a_cont);", "std::exp(-dt * a_cont);"),
+    ("decay_sign", "const double abar = std::exp(dt * a_cont);\n      const double bbar",
+     "const double abar = std::exp(-dt * a_cont);\n      const double bbar"),
     ("no_decay", "h[n] = abar * h[n] + bbar * u;", "h[n] = h[n] + bbar * u;"),
     ("drop_skip", "acc + dskip * u;", "acc;"),
     ("skip_on_x", "acc + dskip * u;", "acc + dskip * p.x[(b * L + t) * D + d];"),
@@ -26,8 +27,8 @@ MUTANTS = [
      "acc += Ct[n] * h[n];\n      h[n] = abar * h[n] + bbar * u;"),
     ("delta_lag", "double v = p.delta[(b * p.seqlen + t) * p.dim + d];",
      "double v = p.delta[(b * p.seqlen + (t > 0 ? t - 1 : 0)) * p.dim + d];"),
-    ("A_transposed", "const double a_cont = p.A[d * N + n];",
-     "const double a_cont = p.A[(n * D + d) % (D * N)];"),
+    ("A_transposed", "const double a_cont = p.A[d * N + n];\n      const double abar",
+     "const double a_cont = p.A[(n * D + d) % (D * N)];\n      const double abar"),
     ("conv_flipped", "const int64_t src = t - (K - 1) + k;", "const int64_t src = t - k;"),
     ("conv_no_bias", "double z = p.conv_b ? p.conv_b[d] : 0.0;", "double z = 0.0;"),
     ("silu_sign", "return z / (1.0 + std::exp(-z));", "return z / (1.0 + std::exp(z));"),
@@ -49,6 +50,20 @@ MUTANTS = [
     ("conv_state_reversed", "return p.conv_state_in[(b * p.dim + d) * S + S + t];",
      "return p.conv_state_in[(b * p.dim + d) * S - 1 - t];"),
     ("conv_state_out_shift", "x_at(p, b, L - S + j, d);", "x_at(p, b, L - S + j - 1, d);"),
+    ("bwd_no_adjoint_decay", "g[n] = abar * G;", "g[n] = G;"),
+    ("bwd_drop_output_term", "const double G = g[n] + Cn * gy;", "const double G = g[n];"),
+    ("bwd_dC_prev_state", "p.dC[(b * L + t) * N + n] += gy * h_now;",
+     "p.dC[(b * L + t) * N + n] += gy * h_prev;"),
+    ("bwd_ddelta_no_decay_term", "ddt += G * (a_cont * abar * h_prev + df_dt * Bn * u);",
+     "ddt += G * (df_dt * Bn * u);"),
+    ("bwd_dA_no_input_term", "dA[d * N + n] += G * (dt * abar * h_prev + df_da * Bn * u);",
+     "dA[d * N + n] += G * (dt * abar * h_prev);"),
+    ("bwd_zoh_dfda_sign", "*df_da = (dt * e - std::expm1(dt * a_cont) / a_cont) / a_cont;",
+     "*df_da = (std::expm1(dt * a_cont) / a_cont - dt * e) / a_cont;"),
+    ("bwd_du_no_factor", "du += G * f * Bn;", "du += G * Bn;"),
+    ("bwd_dD_no_input", "dD[d] += gy * u;", "dD[d] += gy;"),
+    ("bwd_dh0_undecayed", "for (int64_t n = 0; n < N; ++n) p.dh0[(b * D + d) * N + n] = g[n];",
+     "for (int64_t n = 0; n < N; ++n) p.dh0[(b * D + d) * N + n] = g[n] + 1e-3;"),
 ]
 
 
