@@ -171,6 +171,45 @@ typedef struct {
                                          end with x); required when conv_w is given and K > 1 */
 } ssm_step_args_t;
 
+/* Backward selective scan: gradients of
+ *   loss = sum(dy * y) + sum(dh_last * h_last)
+ * for ssm_scan_fwd without fused steps (no conv prologue, Delta as given, no
+ * gate).  The derivative of the recurrence defined above (the pages name
+ * training as the purpose of the parallel scan -- explainer, section "3.6
+ * Empirical Evaluation"; VMamba note, section "硬件感知的设计" -- and print
+ * no gradient formula; the chain rule of the definition is the reading):
+ *   g_t = C_t dy_t + Abar_{t+1} g_{t+1} (g_{L-1} also receives dh_last),
+ *   dx_t = sum_n g_t f_t B_t + Dskip dy_t, dDelta_t, dA, dB, dC, dD, dh0.
+ * All gradients are fp32 and overwritten (not accumulated).  Inputs are as
+ * in ssm_scan_args_t; dy has in_dtype.  The adjoint is chunked like the
+ * forward scan and the forward states are recomputed, so nothing of size
+ * batch x L x D x N is stored. */
+typedef struct {
+  int64_t batch, seqlen, dim, dstate; /* Bt, L, D, N */
+  int32_t in_dtype;                   /* ssm_dtype_t of x, delta, Bm, Cm, dy */
+  int32_t disc;                       /* ssm_disc_t */
+  int32_t super_chunk;                /* steps per adjoint chunk (multiple of 16); 0 = plan */
+  int32_t reserved;                   /* must be 0 */
+  const void* x;                      /* (Bt, L, D) */
+  const void* delta;                  /* (Bt, L, D) */
+  const float* A;                     /* (D, N) */
+  const void* Bm;                     /* (Bt, L, N) */
+  const void* Cm;                     /* (Bt, L, N) */
+  const float* Dskip;                 /* (D) or NULL */
+  const float* h0;                    /* (Bt, D, N) or NULL */
+  const void* dy;                     /* (Bt, L, D) gradient of y */
+  const float* dh_last;               /* (Bt, D, N) gradient of h_last, or NULL */
+  float* dx;                          /* (Bt, L, D) */
+  float* ddelta;                      /* (Bt, L, D) */
+  float* dA;                          /* (D, N) */
+  float* dB;                          /* (Bt, L, N) */
+  float* dC;                          /* (Bt, L, N) */
+  float* dD;                          /* (D) or NULL */
+  float* dh0;                         /* (Bt, D, N) or NULL */
+  void* workspace;                    /* >= ssm_scan_bwd_workspace_size() bytes */
+  size_t workspace_bytes;
+} ssm_scan_bwd_args_t;
+
 /* Returns SSM_ABI_VERSION. */
 int ssm_abi_version(void);
 
@@ -197,6 +236,15 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_args_t* args, void* hip_stream);
  * and conv_state_in = conv_state_out = conv_state.  y must not overlap h,
  * conv_state or any input. */
 ssm_status_t ssm_step(const ssm_step_args_t* args, void* hip_stream);
+
+/* Bytes of device workspace ssm_scan_bwd needs (never 0 for a non-empty
+ * problem).  Pure host function; 0 for invalid sizes. */
+size_t ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args_t* args);
+
+/* Backward selective scan (see ssm_scan_bwd_args_t).  Asynchronous on
+ * hip_stream; outputs must not overlap each other, the inputs or the
+ * workspace.  Errors as for ssm_scan_fwd. */
+ssm_status_t ssm_scan_bwd(const ssm_scan_bwd_args_t* args, void* hip_stream);
 
 /* Static description of a status code. */
 const char* ssm_status_string(ssm_status_t status);

@@ -79,8 +79,26 @@ class StepArgs(ctypes.Structure):
     ]
 
 
+class BwdArgs(ctypes.Structure):
+    """Mirror of ssm_scan_bwd_args_t."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+        ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+        ("in_dtype", ctypes.c_int32), ("disc", ctypes.c_int32),
+        ("super_chunk", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("delta", ctypes.c_void_p), ("A", ctypes.c_void_p),
+        ("Bm", ctypes.c_void_p), ("Cm", ctypes.c_void_p), ("Dskip", ctypes.c_void_p),
+        ("h0", ctypes.c_void_p), ("dy", ctypes.c_void_p), ("dh_last", ctypes.c_void_p),
+        ("dx", ctypes.c_void_p), ("ddelta", ctypes.c_void_p), ("dA", ctypes.c_void_p),
+        ("dB", ctypes.c_void_p), ("dC", ctypes.c_void_p), ("dD", ctypes.c_void_p),
+        ("dh0", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 EXPORTS = ["ssm_abi_version", "ssm_scan_workspace_size", "ssm_scan_plan_chunk_len",
-           "ssm_scan_fwd", "ssm_step", "ssm_status_string", "ssm_last_error_message"]
+           "ssm_scan_fwd", "ssm_step", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd",
+           "ssm_status_string", "ssm_last_error_message"]
 
 _lib = None
 
@@ -104,6 +122,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssm_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), ctypes.c_void_p]
     lib.ssm_step.restype = ctypes.c_int
     lib.ssm_step.argtypes = [ctypes.POINTER(StepArgs), ctypes.c_void_p]
+    lib.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdArgs)]
+    lib.ssm_scan_bwd.restype = ctypes.c_int
+    lib.ssm_scan_bwd.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_status_string.argtypes = [ctypes.c_int]
     lib.ssm_last_error_message.restype = ctypes.c_char_p
@@ -411,3 +433,73 @@ def step(h, x, delta, A, B, C, D=None, zoh=False, y=None, out_dtype=None, stream
     status = lib.ssm_step(ctypes.byref(args), _stream_handle(stream))
     _raise_for(lib, status)
     return y
+
+
+def make_bwd_args(x, delta, A, B, C, dy, D=None, h0=None, dh_last=None, zoh=False, grads=None,
+                  super_chunk=0) -> BwdArgs:
+    """Fill a BwdArgs; ``grads`` is the dict of float32 gradient tensors
+    (dx, ddelta, dA, dB, dC and optionally dD, dh0)."""
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be (batch, L, dim) and A (dim, N)")
+    batch, L, dim = x.shape
+    N = A.shape[1]
+    a = BwdArgs()
+    a.batch, a.seqlen, a.dim, a.dstate = batch, L, dim, N
+    a.in_dtype = _dtype_code(x)
+    for name, t in (("delta", delta), ("B", B), ("C", C), ("dy", dy)):
+        if _dtype_code(t) != a.in_dtype:
+            raise ValueError("%s must have the dtype of x" % name)
+    if tuple(delta.shape) != tuple(x.shape) or tuple(dy.shape) != tuple(x.shape):
+        raise ValueError("delta and dy must have the shape of x")
+    if tuple(B.shape) != (batch, L, N) or tuple(C.shape) != (batch, L, N):
+        raise ValueError("B and C must be (batch, L, N)")
+    if D is not None and tuple(D.shape) != (dim,):
+        raise ValueError("D must be (dim,)")
+    for name, t in (("h0", h0), ("dh_last", dh_last)):
+        if t is not None and tuple(t.shape) != (batch, dim, N):
+            raise ValueError("%s must be (batch, dim, N)" % name)
+    shapes = {"dx": (batch, L, dim), "ddelta": (batch, L, dim), "dA": (dim, N),
+              "dB": (batch, L, N), "dC": (batch, L, N), "dD": (dim,), "dh0": (batch, dim, N)}
+    for k, t in grads.items():
+        if t is not None and tuple(t.shape) != shapes[k]:
+            raise ValueError("%s must be %s" % (k, shapes[k]))
+        setattr(a, k, _ptr(_f32(t, k)))
+    a.disc = SSM_DISC_ZOH if zoh else SSM_DISC_DELTA_B
+    a.super_chunk = int(super_chunk)
+    a.x, a.delta, a.A, a.Bm, a.Cm = _ptr(x), _ptr(delta), _ptr(_f32(A, "A")), _ptr(B), _ptr(C)
+    a.Dskip = _ptr(_f32(D, "D"))
+    a.h0 = _ptr(_f32(h0, "h0"))
+    a.dy = _ptr(dy)
+    a.dh_last = _ptr(_f32(dh_last, "dh_last"))
+    return a
+
+
+def scan_bwd(x, delta, A, B, C, dy, D=None, h0=None, dh_last=None, zoh=False, want_dD=True,
+             want_dh0=True, super_chunk=0, workspace=None, stream=None) -> dict:
+    """Backward selective scan on the current (or given) stream: the
+    gradients of sum(dy * y) + sum(dh_last * h_last) of ``scan`` (no fused
+    steps).  Returns a dict of float32 tensors dx, ddelta, dA, dB, dC and,
+    when asked, dD and dh0."""
+    torch = _torch()
+    lib = load_library()
+    batch, L, dim = x.shape
+    N = A.shape[1]
+    dev = x.device
+    f32 = torch.float32
+    g = {"dx": torch.empty((batch, L, dim), dtype=f32, device=dev),
+         "ddelta": torch.empty((batch, L, dim), dtype=f32, device=dev),
+         "dA": torch.empty((dim, N), dtype=f32, device=dev),
+         "dB": torch.empty((batch, L, N), dtype=f32, device=dev),
+         "dC": torch.empty((batch, L, N), dtype=f32, device=dev),
+         "dD": torch.empty((dim,), dtype=f32, device=dev) if want_dD else None,
+         "dh0": torch.empty((batch, dim, N), dtype=f32, device=dev) if want_dh0 else None}
+    args = make_bwd_args(x, delta, A, B, C, dy, D, h0, dh_last, zoh, g, super_chunk)
+    need = int(lib.ssm_scan_bwd_workspace_size(ctypes.byref(args)))
+    if need > 0:
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        args.workspace = _ptr(workspace)
+        args.workspace_bytes = workspace.numel()
+    status = lib.ssm_scan_bwd(ctypes.byref(args), _stream_handle(stream))
+    _raise_for(lib, status)
+    return {k: v for k, v in g.items() if v is not None}

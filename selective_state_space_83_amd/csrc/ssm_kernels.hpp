@@ -327,10 +327,11 @@ __device__ __forceinline__ float conv_push(ConvState& cs, float xv) {
 }
 
 // Lane offset within a 64-channel tile, clamped so that lanes past the last
-// channel duplicate channel D - 1.
-__device__ __forceinline__ uint32_t lane_offset(int64_t dbase, int64_t D) {
+// channel duplicate channel D - 1.  `l` is the lane within its wave (the
+// thread index in the one-wave workgroups of the forward kernels).
+__device__ __forceinline__ uint32_t lane_offset(int64_t dbase, int64_t D,
+                                                uint32_t l = threadIdx.x) {
   const int64_t last = D - 1 - dbase;
-  const uint32_t l = threadIdx.x;
   return (static_cast<int64_t>(l) <= last) ? l : static_cast<uint32_t>(last);
 }
 

@@ -10,6 +10,7 @@
 
 #include "ssm_scan.h"
 #include "ssm_kernels.hpp"
+#include "ssm_bwd.hpp"
 
 namespace {
 
@@ -352,6 +353,228 @@ ssm_status_t run_step_n(const ssm_step_args_t* a, const ssmk::StepParams& kp, hi
                                  : run_step_t<N, bf16_t, bf16_t>(a, kp, s);
 }
 
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+
+struct BwdPlan {
+  int64_t Cf = 0;       // 16-step chunks (forward states recomputed from)
+  int64_t Ts = 0;       // super-chunk length
+  int64_t Cs = 0;       // super-chunks
+  int64_t dtiles = 0;
+  size_t off_hcar = 0, off_dsumf = 0, off_gsum = 0, off_dsums = 0, off_dAp = 0, off_dDp = 0,
+         off_dBp = 0, off_dCp = 0, total = 0;
+};
+
+int ng_of(int64_t N) { return N < 4 ? 1 : int(N / 4); }
+
+// Sizes assumed validated.  The main pass targets about kTargetWaves waves.
+BwdPlan make_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t super_chunk) {
+  BwdPlan pl;
+  const int64_t F = ssmk::kBwdFine;
+  pl.dtiles = (D + ssmk::kWave - 1) / ssmk::kWave;
+  if (L == 0 || Bt * D == 0) return pl;
+  pl.Cf = (L + F - 1) / F;
+  int64_t fines;   // fine chunks per super-chunk
+  if (super_chunk > 0) {
+    fines = super_chunk / F;
+  } else {
+    const int64_t waves = Bt * pl.dtiles * ng_of(N);
+    const int64_t cs = std::max<int64_t>(1, std::min<int64_t>(kTargetWaves / waves, pl.Cf));
+    fines = (pl.Cf + cs - 1) / cs;
+  }
+  // the reverse summary addresses a super-chunk's rows with 32-bit offsets
+  const int64_t max_fines = std::max<int64_t>(1, kMaxChunkBytes / (D * 4) / F);
+  fines = std::max<int64_t>(1, std::min(fines, max_fines));
+  pl.Ts = fines * F;
+  pl.Cs = (L + pl.Ts - 1) / pl.Ts;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t bt = size_t(Bt), d = size_t(D), n = size_t(N);
+  pl.off_hcar = take(bt * size_t(pl.Cf - 1) * d * n * 4);
+  pl.off_dsumf = take(bt * size_t(pl.Cf - 1) * d * 4);
+  pl.off_gsum = take(bt * size_t(pl.Cs - 1) * d * n * 4);
+  pl.off_dsums = take(bt * size_t(pl.Cs - 1) * d * 4);
+  pl.off_dAp = take(bt * size_t(pl.Cs) * d * n * 4);
+  pl.off_dDp = take(bt * size_t(pl.Cs) * d * 4);
+  pl.off_dBp = take(bt * size_t(L) * size_t(pl.dtiles) * n * 4);
+  pl.off_dCp = take(bt * size_t(L) * size_t(pl.dtiles) * n * 4);
+  pl.total = off;
+  return pl;
+}
+
+ssm_status_t check_bwd(const ssm_scan_bwd_args_t* a, BwdPlan* plan) {
+  if (!a) return fail(SSM_ERR_NULL, "args is NULL");
+  if (a->batch < 0 || a->seqlen < 0 || a->dim < 0)
+    return fail(SSM_ERR_SHAPE, "negative size: batch=%lld seqlen=%lld dim=%lld",
+                (long long)a->batch, (long long)a->seqlen, (long long)a->dim);
+  if (a->dstate < 1) return fail(SSM_ERR_SHAPE, "dstate must be >= 1 (got %lld)", (long long)a->dstate);
+  if (a->in_dtype != SSM_F32 && a->in_dtype != SSM_BF16)
+    return fail(SSM_ERR_DTYPE, "unknown in_dtype %d", a->in_dtype);
+  if (a->disc != SSM_DISC_DELTA_B && a->disc != SSM_DISC_ZOH)
+    return fail(SSM_ERR_DTYPE, "unknown discretization %d", a->disc);
+  if (!supported_n(a->dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not in {1,2,4,8,16}", (long long)a->dstate);
+  if (a->reserved != 0) return fail(SSM_ERR_UNSUPPORTED, "reserved field must be 0");
+  if (a->super_chunk < 0 || a->super_chunk % ssmk::kBwdFine != 0)
+    return fail(SSM_ERR_UNSUPPORTED, "super_chunk must be a non-negative multiple of %d",
+                ssmk::kBwdFine);
+  int64_t bl, bld, bln, dn, bdn, blt;
+  const int64_t dtiles = (a->dim + ssmk::kWave - 1) / ssmk::kWave;
+  if (!mul_ok(a->batch, a->seqlen, &bl) || !mul_ok(bl, a->dim, &bld) ||
+      !mul_ok(bl, a->dstate, &bln) || !mul_ok(a->dim, a->dstate, &dn) ||
+      !mul_ok(a->batch, dn, &bdn) || !mul_ok(bln, dtiles, &blt) || bld > INT64_MAX / 8 ||
+      blt > INT64_MAX / 8 || bdn > INT64_MAX / 8)
+    return fail(SSM_ERR_SHAPE, "sizes overflow");
+  *plan = make_bwd_plan(a->batch, a->seqlen, a->dim, a->dstate, a->super_chunk);
+  if (!a->A || !a->dA) return fail(SSM_ERR_NULL, "A and dA are required");
+  const bool work = a->seqlen > 0 && a->batch * a->dim > 0;
+  if (work && (!a->x || !a->delta || !a->Bm || !a->Cm || !a->dy || !a->dx || !a->ddelta ||
+               !a->dB || !a->dC))
+    return fail(SSM_ERR_NULL, "x, delta, Bm, Cm, dy, dx, ddelta, dB and dC are required");
+  const size_t in_sz = dtype_size(a->in_dtype);
+  if (misaligned(a->x, in_sz) || misaligned(a->delta, in_sz) || misaligned(a->dy, in_sz) ||
+      misaligned(a->Bm, 4) || misaligned(a->Cm, 4) || misaligned(a->A, 4) ||
+      misaligned(a->Dskip, 4) || misaligned(a->h0, 4) || misaligned(a->dh_last, 4) ||
+      misaligned(a->dx, 4) || misaligned(a->ddelta, 4) || misaligned(a->dA, 4) ||
+      misaligned(a->dB, 4) || misaligned(a->dC, 4) || misaligned(a->dD, 4) ||
+      misaligned(a->dh0, 4) || misaligned(a->workspace, 256))
+    return fail(SSM_ERR_UNSUPPORTED,
+                "misaligned pointer (element alignment; B, C 4 bytes; workspace 256 bytes)");
+  const Range ins[] = {
+      {a->x, size_t(bld) * in_sz},   {a->delta, size_t(bld) * in_sz}, {a->A, size_t(dn) * 4},
+      {a->Bm, size_t(bln) * in_sz},  {a->Cm, size_t(bln) * in_sz},    {a->Dskip, size_t(a->dim) * 4},
+      {a->h0, size_t(bdn) * 4},      {a->dy, size_t(bld) * in_sz},    {a->dh_last, size_t(bdn) * 4},
+  };
+  const Range outs[] = {
+      {a->dx, size_t(bld) * 4}, {a->ddelta, size_t(bld) * 4}, {a->dA, size_t(dn) * 4},
+      {a->dB, size_t(bln) * 4}, {a->dC, size_t(bln) * 4},     {a->dD, size_t(a->dim) * 4},
+      {a->dh0, size_t(bdn) * 4},
+  };
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return fail(SSM_ERR_ALIAS, "a gradient overlaps an input");
+    for (size_t k = i + 1; k < sizeof(outs) / sizeof(outs[0]); ++k)
+      if (overlap(outs[i], outs[k])) return fail(SSM_ERR_ALIAS, "two gradients overlap");
+  }
+  if (!work) return SSM_OK;
+  if (!a->workspace) return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required", plan->total);
+  if (a->workspace_bytes < plan->total)
+    return fail(SSM_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", a->workspace_bytes,
+                plan->total);
+  const Range ws{a->workspace, plan->total};
+  for (const Range& r : ins)
+    if (overlap(ws, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps an input");
+  for (const Range& r : outs)
+    if (overlap(ws, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
+  const int64_t ng = ng_of(a->dstate);
+  if (a->batch * plan->Cf * plan->dtiles > kMaxGrid ||
+      a->batch * plan->Cs * plan->dtiles * ng > kMaxGrid || (bln + 255) / 256 > kMaxGrid ||
+      (bdn + 63) / 64 > kMaxGrid)
+    return fail(SSM_ERR_SHAPE, "problem too large for one launch");
+  return SSM_OK;
+}
+
+template <int N, typename InT, int DISC>
+ssm_status_t run_bwd(const ssm_scan_bwd_args_t* a, const BwdPlan& pl, hipStream_t s) {
+  using namespace ssmk;
+  char* ws = static_cast<char*>(a->workspace);
+  const float thr = exact_threshold(a->disc, a->in_dtype);
+  // forward states entering every 16-step chunk: the forward summary and
+  // carry passes run at that chunk length
+  if (pl.Cf > 1) {
+    ScanParams fp{};
+    fp.x = a->x;
+    fp.delta = a->delta;
+    fp.A = a->A;
+    fp.Bm = a->Bm;
+    fp.Cm = a->Cm;
+    fp.h0 = a->h0;
+    fp.dsum = reinterpret_cast<float*>(ws + pl.off_dsumf);
+    fp.hsum = reinterpret_cast<float*>(ws + pl.off_hcar);
+    fp.Bt = a->batch;
+    fp.L = a->seqlen;
+    fp.D = a->dim;
+    fp.T = kBwdFine;
+    fp.C = pl.Cf;
+    fp.dtiles = int32_t(pl.dtiles);
+    fp.exact_thr = thr;
+    fp.dt_mode = kDtRaw;
+    fp.nwg = int32_t(a->batch * (pl.Cf - 1) * pl.dtiles);
+    hipLaunchKernelGGL((k_chunk_summary<N, InT, DISC, false>), dim3(fp.nwg), dim3(kWave), 0, s, fp);
+    if (ssm_status_t st = launch_status("k_chunk_summary (backward)")) return st;
+    const int64_t chains = a->batch * a->dim * N;
+    hipLaunchKernelGGL((k_carry_combine<N>), dim3(uint32_t((chains + 63) / 64)), dim3(kWave), 0, s,
+                       fp);
+    if (ssm_status_t st = launch_status("k_carry_combine (backward)")) return st;
+  }
+  BwdParams bp{};
+  bp.x = a->x;
+  bp.delta = a->delta;
+  bp.A = a->A;
+  bp.Bm = a->Bm;
+  bp.Cm = a->Cm;
+  bp.Dskip = a->Dskip;
+  bp.h0 = a->h0;
+  bp.dy = a->dy;
+  bp.dh_last = a->dh_last;
+  bp.dx = a->dx;
+  bp.ddelta = a->ddelta;
+  bp.dA = a->dA;
+  bp.dB = a->dB;
+  bp.dC = a->dC;
+  bp.dD = a->dD;
+  bp.dh0 = a->dh0;
+  bp.hcar = reinterpret_cast<const float*>(ws + pl.off_hcar);
+  bp.gsum = reinterpret_cast<float*>(ws + pl.off_gsum);
+  bp.dsum_s = reinterpret_cast<float*>(ws + pl.off_dsums);
+  bp.dAp = reinterpret_cast<float*>(ws + pl.off_dAp);
+  bp.dDp = reinterpret_cast<float*>(ws + pl.off_dDp);
+  bp.dBp = reinterpret_cast<float*>(ws + pl.off_dBp);
+  bp.dCp = reinterpret_cast<float*>(ws + pl.off_dCp);
+  bp.Bt = a->batch;
+  bp.L = a->seqlen;
+  bp.D = a->dim;
+  bp.Ts = pl.Ts;
+  bp.Cs = pl.Cs;
+  bp.Cf = pl.Cf;
+  bp.dtiles = int32_t(pl.dtiles);
+  bp.exact_thr = thr;
+  if (pl.Cs > 1) {
+    bp.nwg = int32_t(a->batch * (pl.Cs - 1) * pl.dtiles);
+    hipLaunchKernelGGL((k_bwd_summary<N, InT, DISC>), dim3(bp.nwg), dim3(kWave), 0, s, bp);
+    if (ssm_status_t st = launch_status("k_bwd_summary")) return st;
+    const int64_t chains = a->batch * a->dim * N;
+    hipLaunchKernelGGL((k_bwd_combine<N>), dim3(uint32_t((chains + 63) / 64)), dim3(kWave), 0, s,
+                       bp);
+    if (ssm_status_t st = launch_status("k_bwd_combine")) return st;
+  }
+  constexpr int NG = BwdLayout<N>::NG;
+  bp.nwg = int32_t(a->batch * pl.Cs * pl.dtiles);
+  hipLaunchKernelGGL((k_bwd_main<N, InT, DISC>), dim3(bp.nwg), dim3(kWave * NG), 0, s, bp);
+  if (ssm_status_t st = launch_status("k_bwd_main")) return st;
+  const int64_t nbc = a->batch * a->seqlen * N;
+  hipLaunchKernelGGL((k_bwd_reduce_bc<N>), dim3(uint32_t((nbc + 255) / 256)), dim3(256), 0, s, bp);
+  if (ssm_status_t st = launch_status("k_bwd_reduce_bc")) return st;
+  const int64_t nad = a->dim * N + a->dim;
+  hipLaunchKernelGGL((k_bwd_reduce_ad<N>), dim3(uint32_t((nad + 255) / 256)), dim3(256), 0, s, bp);
+  return launch_status("k_bwd_reduce_ad");
+}
+
+template <int N>
+ssm_status_t run_bwd_n(const ssm_scan_bwd_args_t* a, const BwdPlan& pl, hipStream_t s) {
+  using ssmk::bf16_t;
+  if (a->in_dtype == SSM_F32)
+    return a->disc == SSM_DISC_ZOH ? run_bwd<N, float, ssmk::kZoh>(a, pl, s)
+                                   : run_bwd<N, float, ssmk::kDeltaB>(a, pl, s);
+  return a->disc == SSM_DISC_ZOH ? run_bwd<N, bf16_t, ssmk::kZoh>(a, pl, s)
+                                 : run_bwd<N, bf16_t, ssmk::kDeltaB>(a, pl, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -464,6 +687,52 @@ ssm_status_t ssm_step(const ssm_step_args_t* a, void* hip_stream) {
     case 4: return run_step_n<4>(a, kp, s);
     case 8: return run_step_n<8>(a, kp, s);
     default: return run_step_n<16>(a, kp, s);
+  }
+}
+
+size_t ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args_t* a) {
+  if (!a || a->batch < 0 || a->seqlen < 0 || a->dim < 0 || a->dstate < 1 ||
+      a->super_chunk < 0 || a->super_chunk % ssmk::kBwdFine != 0)
+    return 0;
+  int64_t bl, bld, bln;
+  if (!mul_ok(a->batch, a->seqlen, &bl) || !mul_ok(bl, a->dim, &bld) ||
+      !mul_ok(bl, a->dstate, &bln) || bln > INT64_MAX / 64)
+    return 0;
+  return make_bwd_plan(a->batch, a->seqlen, a->dim, a->dstate, a->super_chunk).total;
+}
+
+ssm_status_t ssm_scan_bwd(const ssm_scan_bwd_args_t* a, void* hip_stream) {
+  g_msg[0] = '\0';
+  BwdPlan pl;
+  if (ssm_status_t st = check_bwd(a, &pl)) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const int64_t DN = a->dim * a->dstate;
+  if (a->seqlen == 0 || a->batch * a->dim == 0) {
+    // no token: dA, dD are zero and the gradient of h0 is dh_last
+    if (DN > 0) {
+      hipLaunchKernelGGL(ssmk::k_state_copy, dim3(uint32_t((DN + 255) / 256)), dim3(256), 0, s,
+                         a->dA, nullptr, DN);
+      if (ssm_status_t st = launch_status("k_state_copy")) return st;
+    }
+    if (a->dD && a->dim > 0) {
+      hipLaunchKernelGGL(ssmk::k_state_copy, dim3(uint32_t((a->dim + 255) / 256)), dim3(256), 0,
+                         s, a->dD, nullptr, a->dim);
+      if (ssm_status_t st = launch_status("k_state_copy")) return st;
+    }
+    const int64_t n = a->batch * DN;
+    if (a->dh0 && n > 0) {
+      hipLaunchKernelGGL(ssmk::k_state_copy, dim3(uint32_t((n + 255) / 256)), dim3(256), 0, s,
+                         a->dh0, a->dh_last, n);
+      if (ssm_status_t st = launch_status("k_state_copy")) return st;
+    }
+    return SSM_OK;
+  }
+  switch (a->dstate) {
+    case 1: return run_bwd_n<1>(a, pl, s);
+    case 2: return run_bwd_n<2>(a, pl, s);
+    case 4: return run_bwd_n<4>(a, pl, s);
+    case 8: return run_bwd_n<8>(a, pl, s);
+    default: return run_bwd_n<16>(a, pl, s);
   }
 }
 

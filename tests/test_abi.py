@@ -48,15 +48,20 @@ LAYOUT_C = r"""
 int main(void) {
   printf("ssm_scan_args_t sizeof %zu\n", sizeof(ssm_scan_args_t));
   printf("ssm_step_args_t sizeof %zu\n", sizeof(ssm_step_args_t));
+  printf("ssm_scan_bwd_args_t sizeof %zu\n", sizeof(ssm_scan_bwd_args_t));
   %FIELDS%
   return 0;
 }
 """
 
 
+STRUCTS = (("ssm_scan_args_t", ssm.ScanArgs), ("ssm_step_args_t", ssm.StepArgs),
+           ("ssm_scan_bwd_args_t", ssm.BwdArgs))
+
+
 def test_struct_layout_matches_header(tmp_path):
     lines = []
-    for T, cls in (("ssm_scan_args_t", ssm.ScanArgs), ("ssm_step_args_t", ssm.StepArgs)):
+    for T, cls in STRUCTS:
         for f, _ in cls._fields_:
             lines.append("F(%s, %s)" % (T, f))
     src = tmp_path / "layout.c"
@@ -71,7 +76,8 @@ def test_struct_layout_matches_header(tmp_path):
         got[(T, f)] = int(v)
     assert got[("ssm_scan_args_t", "sizeof")] == ctypes.sizeof(ssm.ScanArgs)
     assert got[("ssm_step_args_t", "sizeof")] == ctypes.sizeof(ssm.StepArgs)
-    for T, cls in (("ssm_scan_args_t", ssm.ScanArgs), ("ssm_step_args_t", ssm.StepArgs)):
+    assert got[("ssm_scan_bwd_args_t", "sizeof")] == ctypes.sizeof(ssm.BwdArgs)
+    for T, cls in STRUCTS:
         for f, _ in cls._fields_:
             assert got[(T, f)] == getattr(cls, f).offset, (T, f)
 
@@ -435,6 +441,74 @@ def test_step_errors(lib):
     s = valid_step_args()
     s.reserved = 3
     assert step_call(lib, s) == ssm.SSM_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# backward errors and workspace
+# ---------------------------------------------------------------------------
+
+def valid_bwd_args(batch=2, L=64, D=32, N=16):
+    a = ssm.BwdArgs()
+    a.batch, a.seqlen, a.dim, a.dstate = batch, L, D, N
+    a.in_dtype = ssm.SSM_F32
+    base = 0x100000000
+    for i, f in enumerate(["x", "delta", "A", "Bm", "Cm", "Dskip", "h0", "dy", "dh_last", "dx",
+                           "ddelta", "dA", "dB", "dC", "dD", "dh0", "workspace"]):
+        setattr(a, f, base + i * GB)
+    a.workspace_bytes = 1 << 40
+    return a
+
+
+def bwd_call(lib, a):
+    return lib.ssm_scan_bwd(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("field", ["x", "delta", "A", "Bm", "Cm", "dy", "dx", "ddelta", "dA",
+                                   "dB", "dC"])
+def test_bwd_required(lib, field):
+    a = valid_bwd_args()
+    setattr(a, field, None)
+    assert bwd_call(lib, a) == ssm.SSM_ERR_NULL
+
+
+def test_bwd_errors(lib):
+    a = valid_bwd_args()
+    a.super_chunk = 24                     # not a multiple of 16
+    assert bwd_call(lib, a) == ssm.SSM_ERR_UNSUPPORTED
+    a = valid_bwd_args(N=12)
+    assert bwd_call(lib, a) == ssm.SSM_ERR_UNSUPPORTED
+    a = valid_bwd_args()
+    a.reserved = 1
+    assert bwd_call(lib, a) == ssm.SSM_ERR_UNSUPPORTED
+    a = valid_bwd_args()
+    a.disc = 7
+    assert bwd_call(lib, a) == ssm.SSM_ERR_DTYPE
+    a = valid_bwd_args()
+    a.dx = a.x                             # gradient over an input
+    assert bwd_call(lib, a) == ssm.SSM_ERR_ALIAS
+    a = valid_bwd_args()
+    a.dB = a.dC + 8                        # two gradients overlap
+    assert bwd_call(lib, a) == ssm.SSM_ERR_ALIAS
+    a = valid_bwd_args()
+    a.workspace = a.dA                     # workspace over an output
+    assert bwd_call(lib, a) == ssm.SSM_ERR_ALIAS
+    a = valid_bwd_args()
+    a.workspace_bytes = 16
+    assert bwd_call(lib, a) == ssm.SSM_ERR_WORKSPACE
+    a = valid_bwd_args()
+    a.dy += 2
+    assert bwd_call(lib, a) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_bwd_workspace_size(lib):
+    a = valid_bwd_args(batch=8, L=2048, D=1536, N=16)
+    need = lib.ssm_scan_bwd_workspace_size(ctypes.byref(a))
+    # at least the per-tile dB / dC partials and the 16-step forward carries
+    dtiles = 24
+    assert need >= 2 * 8 * 2048 * dtiles * 16 * 4 + 8 * 127 * 1536 * 16 * 4
+    a.super_chunk = 5
+    assert lib.ssm_scan_bwd_workspace_size(ctypes.byref(a)) == 0
+    assert lib.ssm_scan_bwd_workspace_size(None) == 0
 
 
 # ---------------------------------------------------------------------------
