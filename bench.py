@@ -23,6 +23,12 @@ kernel on the launch stream.  Two roofs are evaluated:
        ZOH, plus 2 slots per (b, t, d) (Delta*u and the skip term).
 The reported bound is the roof with the higher utilisation.
 
+--backward times ssm_scan_bwd instead: the gradients of the same workload's
+scan for upstream gradients dy ~ N(0, 1) and dh_last ~ N(0, 1); the roofline
+entry is that of the main backward kernel k_bwd_main (VALU lane-slots per
+element: 20 for Delta*B, 28 for ZOH -- the forward recompute plus the
+adjoint step, its four gradient products and the channel-sum adds).
+
 --fused runs the same workload with every fused step on: the step size from
 its pre-activation (softplus(delta + bias[d])), the gate y * silu(z) and, with
 a conv, the conv window read from and handed back to a state buffer; the
@@ -112,6 +118,7 @@ def algorithmic_bytes(w, h0=False, h_last=False, fused=False) -> int:
 # VALU lane-slots per (b, t, d) of the fused steps: softplus (bias add, scale,
 # exp (2), 1 + e, compare + select, log (2), 2 muls, sub, rcp (2)) and the
 # gate (scale, exp (2), add, rcp (2), 2 muls)
+SLOTS_BWD_ELEM = {False: 20.0, True: 28.0}   # k_bwd_main, keyed by ZOH
 SLOTS_SOFTPLUS = 15.0
 SLOTS_GATE = 8.0
 
@@ -266,6 +273,35 @@ def bench_decode(w, steps, warmup, torch, ssm, fused=False):
     return dict(total_ms=e0.elapsed_time(e1), wall_s=wall, launch_us=launch_us)
 
 
+def bench_bwd(w, steps, warmup, torch, ssm):
+    import ssm_inputs as SI
+    inp = SI.scan_inputs(w, h0=True)
+    gi = SI.grad_inputs(w)
+    t = {k: to_dev(inp[k], w.in_dtype, torch) for k in ("x", "delta", "B", "C")}
+    A, Dv, h0 = (to_dev(inp[k], "f32", torch) for k in ("A", "D", "h0"))
+    dy = to_dev(gi["dy"], w.in_dtype, torch)
+    dhl = to_dev(gi["dh_last"], "f32", torch)
+    prep, _ = ssm.prepare_bwd(t["x"], t["delta"], A, t["B"], t["C"], dy, D=Dv, h0=h0,
+                              dh_last=dhl, zoh=w.zoh)
+    hip = HipEvents()
+    evs = hip.create(2 * steps)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        prep.run(stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        prep.run(stream, events=(evs[2 * i], evs[2 * i + 1]))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    main_ms = [hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)]
+    hip.destroy(evs)
+    return dict(total_ms=e0.elapsed_time(e1), main_ms=main_ms,
+                super_chunk=None)
+
+
 def cpu_baseline(w, inp, budget_s=20.0):
     """The oracle, untuned, on this host's cores: whole batch rows of the same
     workload, as many as fit the CPU budget (at least one)."""
@@ -301,6 +337,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward scan (ssm_scan_bwd) of the workload")
     ap.add_argument("--fused", action="store_true",
                     help="run with the fused steps on (softplus step size, gate, conv window)")
     ap.add_argument("--chunk-len", type=int, default=0,
@@ -359,6 +397,26 @@ def main():
                           "in_dtype": w.in_dtype, "state": "f32",
                           "fused": "softplus+gate+conv4" if args.fused else None},
                "hbm_gbps": bytes_ / (ms * 1e-3) / 1e9,
+               "roofline": roof, "cpu_baseline": None}
+        print(json.dumps(out), flush=True)
+        return
+
+    if args.backward:
+        r = bench_bwd(w, args.steps, args.warmup, torch, ssm)
+        ms = r["total_ms"] / args.steps
+        main_us = float(np.mean(r["main_ms"])) * 1e3
+        slots = w.elems * SLOTS_BWD_ELEM[w.zoh]
+        alu = slots / (main_us * 1e-6) / 1e12
+        roof = {"bound": "alu", "achieved": alu, "peak": SLOT_PEAK / 1e12,
+                "unit": "T lane-slot/s", "frac": alu / (SLOT_PEAK / 1e12), "traffic": None,
+                "kernel": "k_bwd_main", "kernel_us": main_us}
+        out = {"metric": METRIC, "value": w.elems / (ms * 1e-3), "unit": "elem/s", "n_gpus": 1,
+               "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+               "dtype": "f32", "data": "synthetic",
+               "config": {"workload": w.name, "pass": "backward", "batch": w.batch,
+                          "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
+                          "in_dtype": w.in_dtype, "disc": "zoh" if w.zoh else "delta_b"},
                "roofline": roof, "cpu_baseline": None}
         print(json.dumps(out), flush=True)
         return

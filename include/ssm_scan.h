@@ -208,6 +208,8 @@ typedef struct {
   float* dh0;                         /* (Bt, D, N) or NULL */
   void* workspace;                    /* >= ssm_scan_bwd_workspace_size() bytes */
   size_t workspace_bytes;
+  void* ev_main_start;                /* optional hipEvent_t recorded on hip_stream right */
+  void* ev_main_stop;                 /* before / after the main backward kernel; NULL = none */
 } ssm_scan_bwd_args_t;
 
 /* Returns SSM_ABI_VERSION. */

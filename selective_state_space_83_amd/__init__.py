@@ -93,6 +93,7 @@ class BwdArgs(ctypes.Structure):
         ("dB", ctypes.c_void_p), ("dC", ctypes.c_void_p), ("dD", ctypes.c_void_p),
         ("dh0", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("ev_main_start", ctypes.c_void_p), ("ev_main_stop", ctypes.c_void_p),
     ]
 
 
@@ -474,6 +475,57 @@ def make_bwd_args(x, delta, A, B, C, dy, D=None, h0=None, dh_last=None, zoh=Fals
     return a
 
 
+class PreparedBwd:
+    """A backward scan whose arguments are checked and marshalled once (see
+    PreparedScan); ``run()`` only launches."""
+
+    def __init__(self, args: BwdArgs, keep: tuple):
+        self.args = args
+        self._keep = keep
+        self._lib = load_library()
+
+    def run(self, stream=None, events=None):
+        if events is not None:
+            self.args.ev_main_start, self.args.ev_main_stop = events
+        else:
+            self.args.ev_main_start = self.args.ev_main_stop = None
+        status = self._lib.ssm_scan_bwd(ctypes.byref(self.args), _stream_handle(stream))
+        _raise_for(self._lib, status)
+
+
+def _bwd_outputs(x, A, want_dD, want_dh0):
+    torch = _torch()
+    batch, L, dim = x.shape
+    N = A.shape[1]
+    dev = x.device
+    f32 = torch.float32
+    return {"dx": torch.empty((batch, L, dim), dtype=f32, device=dev),
+            "ddelta": torch.empty((batch, L, dim), dtype=f32, device=dev),
+            "dA": torch.empty((dim, N), dtype=f32, device=dev),
+            "dB": torch.empty((batch, L, N), dtype=f32, device=dev),
+            "dC": torch.empty((batch, L, N), dtype=f32, device=dev),
+            "dD": torch.empty((dim,), dtype=f32, device=dev) if want_dD else None,
+            "dh0": torch.empty((batch, dim, N), dtype=f32, device=dev) if want_dh0 else None}
+
+
+def prepare_bwd(x, delta, A, B, C, dy, D=None, h0=None, dh_last=None, zoh=False,
+                want_dD=True, want_dh0=True, super_chunk=0, workspace=None):
+    """Allocate the gradients and the workspace, check and marshal once;
+    returns (PreparedBwd, grads dict)."""
+    torch = _torch()
+    lib = load_library()
+    g = _bwd_outputs(x, A, want_dD, want_dh0)
+    args = make_bwd_args(x, delta, A, B, C, dy, D, h0, dh_last, zoh, g, super_chunk)
+    need = int(lib.ssm_scan_bwd_workspace_size(ctypes.byref(args)))
+    if need > 0 and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if need > 0:
+        args.workspace = _ptr(workspace)
+        args.workspace_bytes = workspace.numel()
+    keep = (x, delta, A, B, C, dy, D, h0, dh_last, workspace) + tuple(g.values())
+    return PreparedBwd(args, keep), {k: v for k, v in g.items() if v is not None}
+
+
 def scan_bwd(x, delta, A, B, C, dy, D=None, h0=None, dh_last=None, zoh=False, want_dD=True,
              want_dh0=True, super_chunk=0, workspace=None, stream=None) -> dict:
     """Backward selective scan on the current (or given) stream: the
@@ -482,17 +534,8 @@ def scan_bwd(x, delta, A, B, C, dy, D=None, h0=None, dh_last=None, zoh=False, wa
     when asked, dD and dh0."""
     torch = _torch()
     lib = load_library()
-    batch, L, dim = x.shape
-    N = A.shape[1]
     dev = x.device
-    f32 = torch.float32
-    g = {"dx": torch.empty((batch, L, dim), dtype=f32, device=dev),
-         "ddelta": torch.empty((batch, L, dim), dtype=f32, device=dev),
-         "dA": torch.empty((dim, N), dtype=f32, device=dev),
-         "dB": torch.empty((batch, L, N), dtype=f32, device=dev),
-         "dC": torch.empty((batch, L, N), dtype=f32, device=dev),
-         "dD": torch.empty((dim,), dtype=f32, device=dev) if want_dD else None,
-         "dh0": torch.empty((batch, dim, N), dtype=f32, device=dev) if want_dh0 else None}
+    g = _bwd_outputs(x, A, want_dD, want_dh0)
     args = make_bwd_args(x, delta, A, B, C, dy, D, h0, dh_last, zoh, g, super_chunk)
     need = int(lib.ssm_scan_bwd_workspace_size(ctypes.byref(args)))
     if need > 0:

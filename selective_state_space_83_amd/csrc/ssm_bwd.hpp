@@ -37,6 +37,7 @@ namespace ssmk {
 
 constexpr int kBwdFine = 16;     // recompute chunk (steps held in registers)
 constexpr int kBwdBlock = 4;     // steps per LDS exchange
+constexpr int kBwdHalf = 8;      // steps whose states are held in registers at once
 
 struct BwdParams {
   const void* x;
@@ -82,28 +83,67 @@ __device__ __forceinline__ bool any_exact(const ChanConst<NS, DISC>& cc, float d
   return __builtin_amdgcn_ballot_w64(dv < cc.thr) != 0;
 }
 
-// expm1(z) / A and its derivative in A, given z2 = z log2(e) with z = Delta A,
-// a = exp(z), for one state: ZOH's input factor f and df/dA.  Small |z| use
-// the series f = Delta (1 + z/2 + z^2/6 + z^3/24 + z^4/120) and
-// df/dA = Delta^2 (1/2 + z/3 + z^2/8 + z^3/30 + z^4/144); A = 0 gives the
-// limits Delta and Delta^2 / 2.
-__device__ __forceinline__ void zoh_factor(float z2, float a, float dv, float invA, float& f,
-                                           float& dfda) {
-  const float z = z2 * kLn2;
-  if (fabsf(z) < 0.0625f || invA == 0.0f) {
-    float p = fmaf(z, 1.0f / 120.0f, 1.0f / 24.0f);
-    p = fmaf(z, p, 1.0f / 6.0f);
-    p = fmaf(z, p, 0.5f);
-    p = fmaf(z, p, 1.0f);
-    f = dv * p;
-    float q = fmaf(z, 1.0f / 144.0f, 1.0f / 30.0f);
-    q = fmaf(z, q, 0.125f);
-    q = fmaf(z, q, 1.0f / 3.0f);
-    q = fmaf(z, q, 0.5f);
-    dfda = dv * dv * q;
-  } else {
-    f = (a - 1.0f) * invA;
-    dfda = (dv * a - f) * invA;
+// One backward step of one lane for its NS states: given dy, u, Delta and the
+// states before (hp) and after (hn) the step, accumulate the gradient terms
+// and move the adjoint g to the previous step.  EXACT carries the decay as
+// expm1 (slow decay); SERIES (some state of the wave has |z| < 1/16)
+// evaluates ZOH's factor f = expm1(z) / A and df/dA, for the states with
+// small |z| = |Delta A|, by their series:
+//   f = Delta (1 + z/2 + z^2/6 + z^3/24 + z^4/120),
+//   df/dA = Delta^2 (1/2 + z/3 + z^2/8 + z^3/30 + z^4/144),
+// which also give the A = 0 limits; (a - 1) / A and (Delta a - f) / A lose
+// relative precision there.  Both choices are wave-uniform.
+template <int NS, int DISC, bool EXACT, bool SERIES>
+__device__ __forceinline__ void bwd_lane_step(float (&g)[NS], float (&dA)[NS],
+                                              const ChanConst<NS, DISC>& cc, const float (&Av)[NS],
+                                              const float (&Bv)[NS], const float (&Cv)[NS],
+                                              const float (&hp)[NS], const float (&hn)[NS],
+                                              float u, float dv, float dyv, float valid,
+                                              float (&pB)[NS], float (&pC)[NS], float& du,
+                                              float& ddt) {
+  float gb = 0.0f;   // sum_n G B (Delta*B: du and dDelta's input term are Delta, u times it)
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    const float z2 = dv * cc.A2[n];
+    const float a = exp2_fast(z2);
+    const float G = fmaf(Cv[n], dyv, g[n]);
+    pC[n] = dyv * hn[n] * valid;
+    const float ag = EXACT ? fmaf(expm1_from(z2, a), G, G) : a * G;   // into h_{t-1}
+    if constexpr (DISC == kDeltaB) {
+      pB[n] = G * (dv * u) * valid;
+      gb = fmaf(G, Bv[n], gb);
+      ddt = fmaf(ag, Av[n] * hp[n], ddt);
+      dA[n] = fmaf(ag, dv * hp[n], dA[n]);
+    } else {
+      float f = (a - 1.0f) * cc.invA[n];
+      float dfda = fmaf(dv, a, -f) * cc.invA[n];
+      if constexpr (SERIES) {
+        // some state of the wave has |z| < 1/16: the series there, the direct
+        // forms elsewhere (the series is truncated for small |z| only)
+        const float z = z2 * kLn2;
+        float q1 = fmaf(z, 1.0f / 120.0f, 1.0f / 24.0f);
+        q1 = fmaf(z, q1, 1.0f / 6.0f);
+        q1 = fmaf(z, q1, 0.5f);
+        q1 = fmaf(z, q1, 1.0f);
+        float q2 = fmaf(z, 1.0f / 144.0f, 1.0f / 30.0f);
+        q2 = fmaf(z, q2, 0.125f);
+        q2 = fmaf(z, q2, 1.0f / 3.0f);
+        q2 = fmaf(z, q2, 0.5f);
+        const bool small = fabsf(z) < 0.0625f || cc.invA[n] == 0.0f;
+        f = small ? dv * q1 : f;
+        dfda = small ? (dv * dv) * q2 : dfda;
+      }
+      const float Bu = Bv[n] * u;
+      pB[n] = G * (f * u) * valid;
+      du = fmaf(G * f, Bv[n], du);
+      ddt = fmaf(ag, fmaf(Av[n], hp[n], Bu), ddt);   // df/dDelta = a
+      dA[n] = fmaf(ag, dv * hp[n], fmaf(G * dfda, Bu, dA[n]));
+    }
+    g[n] = ag;
+  }
+  if constexpr (DISC == kDeltaB) {
+    du = fmaf(dv, gb, du);
+    ddt = fmaf(u, gb, ddt);
   }
 }
 
@@ -156,13 +196,19 @@ k_bwd_summary(const BwdParams p) {
     const InT* nc = Crow - (has_next ? N : 0);
     if constexpr (N >= 2) asm volatile("" : "+s"(nc) : "s"(Ccur[0]));
     load_row<N>(Cnext, nc);
-    const bool exact = any_exact<N, DISC>(cc, dv);
+    if (any_exact<N, DISC>(cc, dv)) {   // wave-uniform, as in the forward pass
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-      const float z2 = dv * cc.A2[n];
-      const float a = exp2_fast(z2);
-      const float G = fmaf(Ccur[n], dyv, g[n]);
-      g[n] = exact ? fmaf(expm1_from(z2, a), G, G) : a * G;
+      for (int n = 0; n < N; ++n) {
+        const float z2 = dv * cc.A2[n];
+        const float G = fmaf(Ccur[n], dyv, g[n]);
+        g[n] = fmaf(expm1_from(z2, exp2_fast(z2)), G, G);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        const float G = fmaf(Ccur[n], dyv, g[n]);
+        g[n] = exp2_fast(dv * cc.A2[n]) * G;
+      }
     }
     Crow -= N;
     const float yv = dv - dcomp;
@@ -243,7 +289,8 @@ template <int N, typename InT, int DISC>
 __global__ void __launch_bounds__(kWave * BwdLayout<N>::NG) __attribute__((amdgpu_waves_per_eu(4)))
 k_bwd_main(const BwdParams p) {
   constexpr int NS = BwdLayout<N>::NS, NG = BwdLayout<N>::NG;
-  constexpr int F = kBwdFine, K = kBwdBlock;
+  constexpr int F = kBwdFine, K = kBwdBlock, H = kBwdHalf;
+  static_assert(F % H == 0 && H % K == 0, "halves hold whole blocks");
   // LDS: per wave the dB / dC products of one block, [kind][step][state][lane];
   // per workgroup the du / dDelta partials, [kind][wave][step][lane]
   __shared__ float red[NG][2][K][NS][kWave];
@@ -254,7 +301,9 @@ k_bwd_main(const BwdParams p) {
   const int64_t r = wg / p.dtiles;
   const int64_t s = r % p.Cs;
   const int64_t b = r / p.Cs;
-  const int w = threadIdx.x / kWave;
+  // the wave index is uniform across the wave: say so, so that everything
+  // derived from it (the B / C row addresses) stays in SGPRs
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   const int lane = threadIdx.x % kWave;
   const int64_t dbase = dtile * kWave;
   const int64_t d = dbase + lane_offset(dbase, p.D, static_cast<uint32_t>(lane));
@@ -267,6 +316,15 @@ k_bwd_main(const BwdParams p) {
 #pragma unroll
   for (int n = 0; n < NS; ++n) Av[n] = cc.A2[n] * kLn2;
   const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
+  // ZOH's factor is taken from its series when some |Delta A[n]| of the wave
+  // is below 1/16 (where (a - 1) / A would lose relative precision)
+  float zoh_thr = 0.0f;
+  if constexpr (DISC == kZoh) {
+    float amin = __builtin_inff();
+#pragma unroll
+    for (int n = 0; n < NS; ++n) amin = fminf(amin, fabsf(Av[n]));
+    zoh_thr = amin > 0.0f ? 0.0625f / amin : __builtin_inff();
+  }
 
   // adjoint entering the end of this super-chunk
   float g[NS];
@@ -311,74 +369,118 @@ k_bwd_main(const BwdParams p) {
     const InT* Bc = Bp + (b * p.L + t0) * N + n0;
     const InT* Cc = Cp + (b * p.L + t0) * N + n0;
     // forward state entering the chunk
-    float h[NS];
+    float h0c[NS];
     {
       const float* src = (c == 0) ? (p.h0 ? p.h0 + (b * p.D + d) * N + n0 : nullptr)
                                   : p.hcar + ((b * (p.Cf - 1) + c - 1) * p.D + d) * N + n0;
 #pragma unroll
-      for (int n = 0; n < NS; ++n) h[n] = src ? src[n] : 0.0f;
+      for (int n = 0; n < NS; ++n) h0c[n] = src ? src[n] : 0.0f;
     }
-    // recompute the chunk, keeping the state before every step
-    float stash[F][NS];
+    // The chunk is walked back as two halves of H steps, the later half
+    // first.  Each half is recomputed forwards from the chunk's entry state
+    // (the later half after running through the earlier one), keeping the
+    // state before each of its steps: H steps of NS states in registers.
 #pragma unroll
-    for (int j = 0; j < F; ++j) {
+    for (int half = F / H - 1; half >= 0; --half) {
+      const int j0 = half * H;
+      if (j0 >= len) continue;   // wave-uniform
+      const int hlen = (len - j0 < H) ? len - j0 : H;
+      float h[NS];
 #pragma unroll
-      for (int n = 0; n < NS; ++n) stash[j][n] = h[n];
-      if (j < len) {
-        const float u = ldb(rx, lo_in, j * row_in, kIn);
-        const float dv = ldb(rd, lo_in, j * row_in, kIn);
-        float Bv[NS];
-        load_row<NS>(Bv, Bc + j * N);
-        if (any_exact<NS, DISC>(cc, dv))
-          ssm_step_lane<NS, DISC, false, true>(h, cc, Bv, Bv, u, dv);
-        else
-          ssm_step_lane<NS, DISC, false, false>(h, cc, Bv, Bv, u, dv);
+      for (int n = 0; n < NS; ++n) h[n] = h0c[n];
+      float stash[H][NS];
+      // x / Delta of K steps at a time, the next K requested before the
+      // current K are used (rows past the chunk: buffer loads return 0)
+      float xa[K], da[K];
+#pragma unroll
+      for (int jj = 0; jj < K; ++jj) {
+        xa[jj] = ldb(rx, lo_in, jj * row_in, kIn);
+        da[jj] = ldb(rd, lo_in, jj * row_in, kIn);
       }
-    }
-    // h is now the state after the chunk's last step
-
-    // walk back in blocks of K steps
 #pragma unroll
-    for (int jb = F / K - 1; jb >= 0; --jb) {
+      for (int jb = 0; jb < (j0 + H) / K; ++jb) {
+        float xn[K], dn[K];
+        const int nb = (jb + 1 < (j0 + H) / K) ? jb + 1 : jb;
+#pragma unroll
+        for (int jj = 0; jj < K; ++jj) {
+          xn[jj] = ldb(rx, lo_in, (nb * K + jj) * row_in, kIn);
+          dn[jj] = ldb(rd, lo_in, (nb * K + jj) * row_in, kIn);
+        }
+        float Bb[K][NS];
+#pragma unroll
+        for (int jj = 0; jj < K; ++jj) {
+          const int j = jb * K + jj;
+          load_row<NS>(Bb[jj], Bc + (j < len ? j : len - 1) * N);
+        }
+#pragma unroll
+        for (int jj = 0; jj < K; ++jj) {
+          const int j = jb * K + jj;
+          if (j >= j0) {
+#pragma unroll
+            for (int n = 0; n < NS; ++n) stash[j - j0][n] = h[n];
+          }
+          if (j < len) {
+            if (any_exact<NS, DISC>(cc, da[jj]))
+              ssm_step_lane<NS, DISC, false, true>(h, cc, Bb[jj], Bb[jj], xa[jj], da[jj]);
+            else
+              ssm_step_lane<NS, DISC, false, false>(h, cc, Bb[jj], Bb[jj], xa[jj], da[jj]);
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < K; ++jj) {
+          xa[jj] = xn[jj];
+          da[jj] = dn[jj];
+        }
+      }
+      // h is now the state after the half's last step
+
+    // walk the half back in blocks of K steps
+#pragma unroll
+    for (int jb = (j0 + H) / K - 1; jb >= j0 / K; --jb) {
       if (jb * K >= len) continue;   // wave-uniform
+      // the block's rows, all requested before the first is used
+      float ub[K], db[K], yb[K], Bb[K][NS], Cb[K][NS];
+#pragma unroll
+      for (int jj = 0; jj < K; ++jj) {
+        const int j = jb * K + jj;
+        ub[jj] = ldb(rx, lo_in, j * row_in, kIn);
+        db[jj] = ldb(rd, lo_in, j * row_in, kIn);
+        yb[jj] = ldb(ry, lo_in, j * row_in, kIn);
+        load_row<NS>(Bb[jj], Bc + (j < len ? j : len - 1) * N);
+        load_row<NS>(Cb[jj], Cc + (j < len ? j : len - 1) * N);
+      }
 #pragma unroll
       for (int jj = K - 1; jj >= 0; --jj) {
         const int j = jb * K + jj;
         float pB[NS], pC[NS], du = 0.0f, ddt = 0.0f;
 #pragma unroll
         for (int n = 0; n < NS; ++n) pB[n] = pC[n] = 0.0f;
+        const float u = ub[jj], dv = db[jj], dyv = yb[jj];
+        const float (&Bv)[NS] = Bb[jj];
+        const float (&Cv)[NS] = Cb[jj];
         if (j < len) {
-          const float u = ldb(rx, lo_in, j * row_in, kIn);
-          const float dv = ldb(rd, lo_in, j * row_in, kIn);
-          const float dyv = ldb(ry, lo_in, j * row_in, kIn);
-          float Bv[NS], Cv[NS];
-          load_row<NS>(Bv, Bc + j * N);
-          load_row<NS>(Cv, Cc + j * N);
-          const bool last = (j == len - 1);
-          const bool exact = any_exact<NS, DISC>(cc, dv);
+          const int js = j - j0;                    // index within the half
+          const bool last = (js == hlen - 1);
+          float hn[NS];
 #pragma unroll
-          for (int n = 0; n < NS; ++n) {
-            const float hp = stash[j][n];
-            const float hn = last ? h[n] : stash[j + 1 < F ? j + 1 : j][n];
-            const float z2 = dv * cc.A2[n];
-            const float a = exp2_fast(z2);
-            const float G = fmaf(Cv[n], dyv, g[n]);
-            pC[n] = dyv * hn * valid;
-            float f, dfdt, dfda;
-            if constexpr (DISC == kDeltaB) {
-              f = dv;
-              dfdt = 1.0f;
-              dfda = 0.0f;
-            } else {
-              zoh_factor(z2, a, dv, cc.invA[n], f, dfda);
-              dfdt = a;
-            }
-            pB[n] = G * f * u * valid;
-            du = fmaf(G * f, Bv[n], du);
-            const float ag = exact ? fmaf(expm1_from(z2, a), G, G) : a * G;   // into h_{t-1}
-            ddt = fmaf(ag, Av[n] * hp, fmaf(G * dfdt, Bv[n] * u, ddt));
-            dAacc[n] = fmaf(ag, dv * hp, fmaf(G * dfda, Bv[n] * u, dAacc[n]));
-            g[n] = ag;
+          for (int n = 0; n < NS; ++n) hn[n] = last ? h[n] : stash[js + 1 < H ? js + 1 : js][n];
+          // wave-uniform forms: slow decay, and (ZOH) small |Delta A| series
+          const bool exact = any_exact<NS, DISC>(cc, dv);
+          const bool series = DISC == kZoh && __builtin_amdgcn_ballot_w64(dv < zoh_thr) != 0;
+          if (exact) {
+            if (series)
+              bwd_lane_step<NS, DISC, true, true>(g, dAacc, cc, Av, Bv, Cv, stash[js], hn, u,
+                                                  dv, dyv, valid, pB, pC, du, ddt);
+            else
+              bwd_lane_step<NS, DISC, true, false>(g, dAacc, cc, Av, Bv, Cv, stash[js], hn, u,
+                                                   dv, dyv, valid, pB, pC, du, ddt);
+          } else {
+            if (series)
+              bwd_lane_step<NS, DISC, false, true>(g, dAacc, cc, Av, Bv, Cv, stash[js], hn, u,
+                                                   dv, dyv, valid, pB, pC, du, ddt);
+            else
+              bwd_lane_step<NS, DISC, false, false>(g, dAacc, cc, Av, Bv, Cv, stash[js], hn, u,
+                                                    dv, dyv, valid, pB, pC, du, ddt);
           }
           if (w == 0) dDacc = fmaf(dyv, u, dDacc);
         }
@@ -405,7 +507,7 @@ k_bwd_main(const BwdParams p) {
         acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xF, 0xF, false));
         if (q < Q && half == 0) {
           const int kind = q / (K * NS);
-          const int jj = (q / NS) % K;
+          const int jj = (q % (K * NS)) / NS;
           const int n = q % NS;
           const int j = jb * K + jj;
           if (j < len) {
@@ -431,6 +533,7 @@ k_bwd_main(const BwdParams p) {
         }
       }
       __syncthreads();
+    }
     }
   }
   const int64_t slot = b * p.Cs + s;

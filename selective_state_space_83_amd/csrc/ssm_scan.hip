@@ -368,7 +368,7 @@ struct BwdPlan {
 
 int ng_of(int64_t N) { return N < 4 ? 1 : int(N / 4); }
 
-// Sizes assumed validated.  The main pass targets about kTargetWaves waves.
+// Sizes assumed validated.
 BwdPlan make_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t super_chunk) {
   BwdPlan pl;
   const int64_t F = ssmk::kBwdFine;
@@ -379,7 +379,10 @@ BwdPlan make_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t super
   if (super_chunk > 0) {
     fines = super_chunk / F;
   } else {
-    const int64_t waves = Bt * pl.dtiles * ng_of(N);
+    // the reverse summary runs one wave per (batch row, tile, super-chunk):
+    // enough super-chunks to give it about kTargetWaves waves (the main pass,
+    // with N / 4 waves each, then has more)
+    const int64_t waves = Bt * pl.dtiles;
     const int64_t cs = std::max<int64_t>(1, std::min<int64_t>(kTargetWaves / waves, pl.Cf));
     fines = (pl.Cf + cs - 1) / cs;
   }
@@ -555,8 +558,12 @@ ssm_status_t run_bwd(const ssm_scan_bwd_args_t* a, const BwdPlan& pl, hipStream_
   }
   constexpr int NG = BwdLayout<N>::NG;
   bp.nwg = int32_t(a->batch * pl.Cs * pl.dtiles);
+  hipEvent_t e0 = static_cast<hipEvent_t>(a->ev_main_start);
+  hipEvent_t e1 = static_cast<hipEvent_t>(a->ev_main_stop);
+  if (e0 && hipEventRecord(e0, s) != hipSuccess) return fail(SSM_ERR_HIP, "hipEventRecord failed");
   hipLaunchKernelGGL((k_bwd_main<N, InT, DISC>), dim3(bp.nwg), dim3(kWave * NG), 0, s, bp);
   if (ssm_status_t st = launch_status("k_bwd_main")) return st;
+  if (e1 && hipEventRecord(e1, s) != hipSuccess) return fail(SSM_ERR_HIP, "hipEventRecord failed");
   const int64_t nbc = a->batch * a->seqlen * N;
   hipLaunchKernelGGL((k_bwd_reduce_bc<N>), dim3(uint32_t((nbc + 255) / 256)), dim3(256), 0, s, bp);
   if (ssm_status_t st = launch_status("k_bwd_reduce_bc")) return st;

@@ -231,3 +231,13 @@ def fused_inputs(w: Workload, seed: Optional[int] = None, steps: Optional[int] =
         out["conv_w"] = (np.float32(0.5) * _normal(rng, (D, w.conv_k))).astype(np.float32)
         out["conv_b"] = np.zeros(D, dtype=np.float32)
     return out
+
+
+def grad_inputs(w: Workload, seed: Optional[int] = None) -> dict:
+    """Upstream gradients for the backward scan: dy (Bt, L, D) ~ N(0, 1) in
+    the workload's dtype and dh_last (Bt, D, N) ~ N(0, 1) fp32."""
+    if seed is None:
+        seed = SEED_BASE + w.config_id + 700
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return {"dy": _store(_normal(rng, (w.batch, w.seqlen, w.dim)), w.in_dtype),
+            "dh_last": _normal(rng, (w.batch, w.dim, w.dstate))}
