@@ -98,22 +98,24 @@ __device__ __forceinline__ void bwd_lane_step(float (&g)[NS], float (&dA)[NS],
                                               const ChanConst<NS, DISC>& cc, const float (&Av)[NS],
                                               const float (&Bv)[NS], const float (&Cv)[NS],
                                               const float (&hp)[NS], const float (&hn)[NS],
-                                              float u, float dv, float dyv, float valid,
+                                              float u, float dv, float dyv,
                                               float (&pB)[NS], float (&pC)[NS], float& du,
                                               float& ddt) {
   float gb = 0.0f;   // sum_n G B (Delta*B: du and dDelta's input term are Delta, u times it)
+  const float dvu = dv * u;
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
     const float z2 = dv * cc.A2[n];
     const float a = exp2_fast(z2);
     const float G = fmaf(Cv[n], dyv, g[n]);
-    pC[n] = dyv * hn[n] * valid;
+    pC[n] = dyv * hn[n];
     const float ag = EXACT ? fmaf(expm1_from(z2, a), G, G) : a * G;   // into h_{t-1}
+    const float agh = ag * hp[n];                     // shared by dDelta and dA
     if constexpr (DISC == kDeltaB) {
-      pB[n] = G * (dv * u) * valid;
+      pB[n] = G * dvu;
       gb = fmaf(G, Bv[n], gb);
-      ddt = fmaf(ag, Av[n] * hp[n], ddt);
-      dA[n] = fmaf(ag, dv * hp[n], dA[n]);
+      ddt = fmaf(Av[n], agh, ddt);
+      dA[n] = fmaf(dv, agh, dA[n]);
     } else {
       float f = (a - 1.0f) * cc.invA[n];
       float dfda = fmaf(dv, a, -f) * cc.invA[n];
@@ -134,10 +136,10 @@ __device__ __forceinline__ void bwd_lane_step(float (&g)[NS], float (&dA)[NS],
         dfda = small ? (dv * dv) * q2 : dfda;
       }
       const float Bu = Bv[n] * u;
-      pB[n] = G * (f * u) * valid;
+      pB[n] = G * (f * u);
       du = fmaf(G * f, Bv[n], du);
-      ddt = fmaf(ag, fmaf(Av[n], hp[n], Bu), ddt);   // df/dDelta = a
-      dA[n] = fmaf(ag, dv * hp[n], fmaf(G * dfda, Bu, dA[n]));
+      ddt = fmaf(Av[n], agh, fmaf(ag, Bu, ddt));       // df/dDelta = a
+      dA[n] = fmaf(dv, agh, fmaf(G * dfda, Bu, dA[n]));
     }
     g[n] = ag;
   }
@@ -307,7 +309,15 @@ k_bwd_main(const BwdParams p) {
   const int lane = threadIdx.x % kWave;
   const int64_t dbase = dtile * kWave;
   const int64_t d = dbase + lane_offset(dbase, p.D, static_cast<uint32_t>(lane));
-  const float valid = (dbase + lane < p.D) ? 1.0f : 0.0f;   // clamped lanes add nothing
+  const bool valid = dbase + lane < p.D;   // lanes past D duplicate D - 1 and add nothing
+  if (!valid) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int jj = 0; jj < K; ++jj)
+#pragma unroll
+        for (int n = 0; n < NS; ++n) red[w][k][jj][n][lane] = 0.0f;
+  }
   const int n0 = w * NS;
 
   ChanConst<NS, DISC> cc;
@@ -449,6 +459,14 @@ k_bwd_main(const BwdParams p) {
         load_row<NS>(Bb[jj], Bc + (j < len ? j : len - 1) * N);
         load_row<NS>(Cb[jj], Cc + (j < len ? j : len - 1) * N);
       }
+      // keep the row loads here, together (one wait for the block) rather
+      // than sunk next to each step's first use
+      if constexpr (NS == 4) {
+#pragma unroll
+        for (int jj = 0; jj < K; ++jj)
+          asm volatile("" ::"s"(Bb[jj][0]), "s"(Bb[jj][1]), "s"(Bb[jj][2]), "s"(Bb[jj][3]),
+                       "s"(Cb[jj][0]), "s"(Cb[jj][1]), "s"(Cb[jj][2]), "s"(Cb[jj][3]));
+      }
 #pragma unroll
       for (int jj = K - 1; jj >= 0; --jj) {
         const int j = jb * K + jj;
@@ -470,24 +488,26 @@ k_bwd_main(const BwdParams p) {
           if (exact) {
             if (series)
               bwd_lane_step<NS, DISC, true, true>(g, dAacc, cc, Av, Bv, Cv, stash[js], hn, u,
-                                                  dv, dyv, valid, pB, pC, du, ddt);
+                                                  dv, dyv, pB, pC, du, ddt);
             else
               bwd_lane_step<NS, DISC, true, false>(g, dAacc, cc, Av, Bv, Cv, stash[js], hn, u,
-                                                   dv, dyv, valid, pB, pC, du, ddt);
+                                                   dv, dyv, pB, pC, du, ddt);
           } else {
             if (series)
               bwd_lane_step<NS, DISC, false, true>(g, dAacc, cc, Av, Bv, Cv, stash[js], hn, u,
-                                                   dv, dyv, valid, pB, pC, du, ddt);
+                                                   dv, dyv, pB, pC, du, ddt);
             else
               bwd_lane_step<NS, DISC, false, false>(g, dAacc, cc, Av, Bv, Cv, stash[js], hn, u,
-                                                    dv, dyv, valid, pB, pC, du, ddt);
+                                                    dv, dyv, pB, pC, du, ddt);
           }
           if (w == 0) dDacc = fmaf(dyv, u, dDacc);
         }
+        if (valid) {   // lanes past the last channel keep their zero entries
 #pragma unroll
-        for (int n = 0; n < NS; ++n) {
-          red[w][0][jj][n][lane] = pB[n];
-          red[w][1][jj][n][lane] = pC[n];
+          for (int n = 0; n < NS; ++n) {
+            red[w][0][jj][n][lane] = pB[n];
+            red[w][1][jj][n][lane] = pC[n];
+          }
         }
         xch[0][w][jj][lane] = du;
         xch[1][w][jj][lane] = ddt;
@@ -565,21 +585,34 @@ __global__ void __launch_bounds__(256) k_bwd_reduce_bc(const BwdParams p) {
 }
 
 // dA (D, N) and dD (D): sum the per-wave partials over batch rows and
-// super-chunks (one thread per (d, n), and per d for dD).
+// super-chunks.  A workgroup covers 64 consecutive outputs (of dA, then dD);
+// its 16 waves sum every 16th partial each and wave 0 adds the 16 results in
+// a fixed order, so the sum is deterministic.
+constexpr int kRedWaves = 16;
+
 template <int N>
-__global__ void __launch_bounds__(256) k_bwd_reduce_ad(const BwdParams p) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+__global__ void __launch_bounds__(kWave * kRedWaves) k_bwd_reduce_ad(const BwdParams p) {
+  __shared__ float part[kRedWaves][kWave];
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kWave + lane;
   const int64_t DN = p.D * N;
   const int64_t parts = p.Bt * p.Cs;
-  if (i < DN) {
-    float acc = 0.0f;
-    for (int64_t k = 0; k < parts; ++k) acc += p.dAp[k * DN + i];
-    p.dA[i] = acc;
-  } else if (i < DN + p.D && p.dD) {
-    const int64_t dd = i - DN;
-    float acc = 0.0f;
-    for (int64_t k = 0; k < parts; ++k) acc += p.dDp[k * p.D + dd];
-    p.dD[dd] = acc;
+  const bool isA = i < DN;
+  const bool isD = !isA && i < DN + p.D && p.dD;
+  float acc = 0.0f;
+  if (isA) {
+    for (int64_t k = w; k < parts; k += kRedWaves) acc += p.dAp[k * DN + i];
+  } else if (isD) {
+    for (int64_t k = w; k < parts; k += kRedWaves) acc += p.dDp[k * p.D + (i - DN)];
+  }
+  part[w][lane] = acc;
+  __syncthreads();
+  if (w == 0) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kRedWaves; ++v) sum += part[v][lane];
+    if (isA) p.dA[i] = sum;
+    else if (isD) p.dD[i - DN] = sum;
   }
 }
 

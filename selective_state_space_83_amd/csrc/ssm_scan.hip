@@ -568,7 +568,8 @@ ssm_status_t run_bwd(const ssm_scan_bwd_args_t* a, const BwdPlan& pl, hipStream_
   hipLaunchKernelGGL((k_bwd_reduce_bc<N>), dim3(uint32_t((nbc + 255) / 256)), dim3(256), 0, s, bp);
   if (ssm_status_t st = launch_status("k_bwd_reduce_bc")) return st;
   const int64_t nad = a->dim * N + a->dim;
-  hipLaunchKernelGGL((k_bwd_reduce_ad<N>), dim3(uint32_t((nad + 255) / 256)), dim3(256), 0, s, bp);
+  hipLaunchKernelGGL((k_bwd_reduce_ad<N>), dim3(uint32_t((nad + kWave - 1) / kWave)),
+                     dim3(kWave * kRedWaves), 0, s, bp);
   return launch_status("k_bwd_reduce_ad");
 }
 
