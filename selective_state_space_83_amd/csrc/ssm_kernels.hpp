@@ -87,6 +87,10 @@ struct ScanParams {
   const void* z;         // (Bt, L, D) gate or null
   const float* cs_in;    // (Bt, D, conv_k - 1) conv window before token 0, or null
   float* cs_out;         // (Bt, D, conv_k - 1) last conv_k - 1 inputs, or null
+  // grouped carry walk (long chunk chains): G groups of gsz chunks
+  float* gS;             // (Bt, G, D)     group sums of Delta
+  float* gB;             // (Bt, G, D, N)  group end states from zero, then carries into groups
+  int64_t G, gsz;
 };
 
 // How the step size is formed from the given delta values.
@@ -603,6 +607,69 @@ __device__ __forceinline__ float decay_add(float z2, float carry, float b) {
   return fmaf(expm1_from(z2, exp2_fast(z2)), carry, carry + b);
 }
 
+// Exclusive walk over G groups: vals[g] (a group's end state from zero) is
+// replaced by the carry into group g, and carry moves past the group.
+__device__ __forceinline__ void walk_carry_in(float a2, float carry, const float* sums,
+                                              int64_t sstr, float* vals, int64_t vstr, int64_t G) {
+  constexpr int U = 8;
+  int64_t g = 0;
+  for (; g + U <= G; g += U) {
+    float sv[U], bv[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      sv[j] = sums[(g + j) * sstr];
+      bv[j] = vals[(g + j) * vstr];
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      vals[(g + j) * vstr] = carry;
+      carry = decay_add(a2 * sv[j], carry, bv[j]);
+    }
+  }
+  for (; g < G; ++g) {
+    const float bv = vals[g * vstr];
+    vals[g * vstr] = carry;
+    carry = decay_add(a2 * sums[g * sstr], carry, bv);
+  }
+}
+
+// Walk chunks [c0, c1) of one (b, d, n) chain from `carry`:
+//   carry <- exp(A * sum_c Delta) * carry + hsum_c
+// with the loads of 8 chunks issued before they are folded.  WRITE stores
+// each new carry over hsum_c (the carry into chunk c + 1); KAHAN also returns
+// the compensated sum of the chunks' Delta sums in *ssum.
+template <bool WRITE, bool KAHAN>
+__device__ __forceinline__ float walk_chunks(float a2, float carry, const float* ds, int64_t dstr,
+                                             float* hs, int64_t hstr, int64_t c0, int64_t c1,
+                                             float* ssum) {
+  constexpr int U = 8;
+  float sacc = 0.0f, scomp = 0.0f;
+  auto fold = [&](float sv, float hv, int64_t c) {
+    carry = decay_add(a2 * sv, carry, hv);
+    if constexpr (WRITE) hs[c * hstr] = carry;
+    if constexpr (KAHAN) {
+      const float y = sv - scomp;
+      const float t = sacc + y;
+      scomp = (t - sacc) - y;
+      sacc = t;
+    }
+  };
+  int64_t c = c0;
+  for (; c + U <= c1; c += U) {
+    float sv[U], hv[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      sv[j] = ds[(c + j) * dstr];
+      hv[j] = hs[(c + j) * hstr];
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) fold(sv[j], hv[j], c + j);
+  }
+  for (; c < c1; ++c) fold(ds[c * dstr], hs[c * hstr], c);
+  if constexpr (KAHAN) *ssum = sacc - scomp;
+  return carry;
+}
+
 // Pass 2: carries.  One lane per (b, d, n); walks the chunks in order,
 //   carry_0 = h0,  carry_{c+1} = exp(A * sum_c Delta) * carry_c + hsum_c,
 // and overwrites hsum_c with carry_{c+1}, the carry into chunk c + 1.
@@ -615,29 +682,62 @@ __global__ void __launch_bounds__(kWave) k_carry_combine(const ScanParams p) {
   const int64_t dn = idx - b * DN;
   const int64_t d = dn / N;
   const float a2 = p.A[dn] * kLog2e;
-  float carry = p.h0 ? p.h0[idx] : 0.0f;
+  const float carry = p.h0 ? p.h0[idx] : 0.0f;
   const int64_t nc = p.C - 1;
-  const float* ds = p.dsum + b * nc * p.D + d;
-  float* hs = p.hsum + b * nc * DN + dn;
-  constexpr int U = 8;
-  int64_t c = 0;
-  for (; c + U <= nc; c += U) {
-    float sv[U], hv[U];
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      sv[j] = ds[(c + j) * p.D];
-      hv[j] = hs[(c + j) * DN];
-    }
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      carry = decay_add(a2 * sv[j], carry, hv[j]);
-      hs[(c + j) * DN] = carry;
-    }
-  }
-  for (; c < nc; ++c) {
-    carry = decay_add(a2 * ds[c * p.D], carry, hs[c * DN]);
-    hs[c * DN] = carry;
-  }
+  walk_chunks<true, false>(a2, carry, p.dsum + b * nc * p.D + d, p.D, p.hsum + b * nc * DN + dn,
+                           DN, 0, nc, nullptr);
+}
+
+// The same carries for long chains, in three parallel steps over groups of
+// gsz chunks (the operator is associative, so a group can be folded before
+// its carry is known -- 53ai.com explainer, section 3.3):
+//   1. per (b, group, d, n): the group's end state from zero and its sum of
+//      Delta;
+//   2. per (b, d, n): the carry into every group, walking the G groups;
+//   3. per (b, group, d, n): the group's chunks again from its carry,
+//      writing the carries into hsum.
+template <int N>
+__global__ void __launch_bounds__(kWave) k_combine_groups(const ScanParams p) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kWave + threadIdx.x;
+  const int64_t DN = p.D * N;
+  if (idx >= p.Bt * p.G * DN) return;
+  const int64_t bg = idx / DN, dn = idx - bg * DN;
+  const int64_t b = bg / p.G, g = bg - b * p.G;
+  const int64_t d = dn / N;
+  const int64_t nc = p.C - 1;
+  const int64_t c0 = g * p.gsz, c1 = (c0 + p.gsz < nc) ? c0 + p.gsz : nc;
+  float ssum;
+  const float be = walk_chunks<false, true>(p.A[dn] * kLog2e, 0.0f, p.dsum + b * nc * p.D + d,
+                                            p.D, p.hsum + b * nc * DN + dn, DN, c0, c1, &ssum);
+  p.gB[idx] = be;
+  if (dn % N == 0) p.gS[bg * p.D + d] = ssum;
+}
+
+template <int N>
+__global__ void __launch_bounds__(kWave) k_combine_top(const ScanParams p) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kWave + threadIdx.x;
+  const int64_t DN = p.D * N;
+  if (idx >= p.Bt * DN) return;
+  const int64_t b = idx / DN, dn = idx - b * DN;
+  const int64_t d = dn / N;
+  float carry = p.h0 ? p.h0[idx] : 0.0f;
+  // gB[g] (the group's end state from zero) becomes the carry into group g
+  float* gb = p.gB + b * p.G * DN + dn;
+  walk_carry_in(p.A[dn] * kLog2e, carry, p.gS + b * p.G * p.D + d, p.D, gb, DN, p.G);
+}
+
+template <int N>
+__global__ void __launch_bounds__(kWave) k_combine_apply(const ScanParams p) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kWave + threadIdx.x;
+  const int64_t DN = p.D * N;
+  if (idx >= p.Bt * p.G * DN) return;
+  const int64_t bg = idx / DN, dn = idx - bg * DN;
+  const int64_t b = bg / p.G, g = bg - b * p.G;
+  const int64_t d = dn / N;
+  const int64_t nc = p.C - 1;
+  const int64_t c0 = g * p.gsz, c1 = (c0 + p.gsz < nc) ? c0 + p.gsz : nc;
+  walk_chunks<true, false>(p.A[dn] * kLog2e, p.gB[idx], p.dsum + b * nc * p.D + d, p.D,
+                           p.hsum + b * nc * DN + dn, DN, c0, c1, nullptr);
 }
 
 // Pass 3 (or the only pass): scan each chunk from its carry-in, write y, and

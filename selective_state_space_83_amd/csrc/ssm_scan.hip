@@ -48,12 +48,32 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 bool supported_n(int64_t n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; }
 
+// Carry walks over more chunks than this are done in groups (three parallel
+// steps instead of one sequential chain per (b, d, n)).
+constexpr int64_t kGroupWalk = 64;
+
+struct Grouping {
+  int64_t G = 0, gsz = 0;   // groups of gsz chunks (G = 0: one sequential walk)
+};
+
+Grouping grouping(int64_t nc) {
+  Grouping g;
+  if (nc <= kGroupWalk) return g;
+  int64_t G = 1;
+  while (G * G < nc) ++G;
+  g.gsz = (nc + G - 1) / G;
+  g.G = (nc + g.gsz - 1) / g.gsz;
+  return g;
+}
+
 struct Plan {
   int64_t T = 0;       // chunk length
   int64_t C = 0;       // chunks
   int64_t dtiles = 0;  // ceil(D / 64)
+  Grouping grp;        // of the carry walk
   size_t ws_dsum = 0;  // bytes
   size_t ws_hsum = 0;
+  size_t ws_gS = 0, ws_gB = 0;
   size_t ws_total = 0;
 };
 
@@ -80,7 +100,10 @@ Plan make_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t chunk_len) {
   if (pl.C > 1) {
     pl.ws_dsum = align256(size_t(Bt) * size_t(pl.C - 1) * size_t(D) * 4);
     pl.ws_hsum = align256(size_t(Bt) * size_t(pl.C - 1) * size_t(D) * size_t(N) * 4);
-    pl.ws_total = pl.ws_dsum + pl.ws_hsum;
+    pl.grp = grouping(pl.C - 1);
+    pl.ws_gS = align256(size_t(Bt) * size_t(pl.grp.G) * size_t(D) * 4);
+    pl.ws_gB = align256(size_t(Bt) * size_t(pl.grp.G) * size_t(D) * size_t(N) * 4);
+    pl.ws_total = pl.ws_dsum + pl.ws_hsum + pl.ws_gS + pl.ws_gB;
   }
   return pl;
 }
@@ -189,7 +212,8 @@ ssm_status_t check_scan(const ssm_scan_args_t* a, Plan* plan) {
       return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
   }
   const int64_t grid_out = a->batch * plan->C * plan->dtiles;
-  if (grid_out > kMaxGrid || (a->batch * a->dim * a->dstate + 63) / 64 > kMaxGrid)
+  const int64_t walk_lanes = a->batch * a->dim * a->dstate * std::max<int64_t>(1, plan->grp.G);
+  if (grid_out > kMaxGrid || (walk_lanes + 63) / 64 > kMaxGrid)
     return fail(SSM_ERR_SHAPE, "problem too large for one launch");
   return SSM_OK;
 }
@@ -268,6 +292,30 @@ ssm_status_t launch_status(const char* what) {
   return SSM_OK;
 }
 
+// The carry walk of pass 2: kp.dsum / kp.hsum hold C - 1 chunk summaries;
+// with a grouping, kp.gS / kp.gB must point at the group buffers.
+template <int N>
+ssm_status_t launch_combine(ssmk::ScanParams kp, const Grouping& grp, hipStream_t s) {
+  const int64_t chains = kp.Bt * kp.D * N;
+  if (grp.G == 0) {
+    hipLaunchKernelGGL((ssmk::k_carry_combine<N>), dim3(uint32_t((chains + 63) / 64)),
+                       dim3(ssmk::kWave), 0, s, kp);
+    return launch_status("k_carry_combine");
+  }
+  kp.G = grp.G;
+  kp.gsz = grp.gsz;
+  const int64_t lanes = chains * grp.G;
+  hipLaunchKernelGGL((ssmk::k_combine_groups<N>), dim3(uint32_t((lanes + 63) / 64)),
+                     dim3(ssmk::kWave), 0, s, kp);
+  if (ssm_status_t st = launch_status("k_combine_groups")) return st;
+  hipLaunchKernelGGL((ssmk::k_combine_top<N>), dim3(uint32_t((chains + 63) / 64)),
+                     dim3(ssmk::kWave), 0, s, kp);
+  if (ssm_status_t st = launch_status("k_combine_top")) return st;
+  hipLaunchKernelGGL((ssmk::k_combine_apply<N>), dim3(uint32_t((lanes + 63) / 64)),
+                     dim3(ssmk::kWave), 0, s, kp);
+  return launch_status("k_combine_apply");
+}
+
 template <int N, typename InT, typename OutT, int DISC, bool CONV, bool GATE>
 ssm_status_t run_scan(ssmk::ScanParams kp, const Plan& pl, hipStream_t s, hipEvent_t ev0,
                       hipEvent_t ev1) {
@@ -276,10 +324,7 @@ ssm_status_t run_scan(ssmk::ScanParams kp, const Plan& pl, hipStream_t s, hipEve
     hipLaunchKernelGGL((ssmk::k_chunk_summary<N, InT, DISC, CONV>), dim3(kp.nwg), dim3(ssmk::kWave),
                        0, s, kp);
     if (ssm_status_t st = launch_status("k_chunk_summary")) return st;
-    const int64_t chains = kp.Bt * kp.D * N;
-    hipLaunchKernelGGL((ssmk::k_carry_combine<N>), dim3(uint32_t((chains + 63) / 64)),
-                       dim3(ssmk::kWave), 0, s, kp);
-    if (ssm_status_t st = launch_status("k_carry_combine")) return st;
+    if (ssm_status_t st = launch_combine<N>(kp, pl.grp, s)) return st;
   }
   kp.nwg = int32_t(kp.Bt * pl.C * pl.dtiles);
   if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return fail(SSM_ERR_HIP, "hipEventRecord failed");
@@ -362,8 +407,9 @@ struct BwdPlan {
   int64_t Ts = 0;       // super-chunk length
   int64_t Cs = 0;       // super-chunks
   int64_t dtiles = 0;
+  Grouping grp;         // of the 16-step forward carry walk
   size_t off_hcar = 0, off_dsumf = 0, off_gsum = 0, off_dsums = 0, off_dAp = 0, off_dDp = 0,
-         off_dBp = 0, off_dCp = 0, total = 0;
+         off_dBp = 0, off_dCp = 0, off_gS = 0, off_gB = 0, total = 0;
 };
 
 int ng_of(int64_t N) { return N < 4 ? 1 : int(N / 4); }
@@ -406,6 +452,9 @@ BwdPlan make_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t super
   pl.off_dDp = take(bt * size_t(pl.Cs) * d * 4);
   pl.off_dBp = take(bt * size_t(L) * size_t(pl.dtiles) * n * 4);
   pl.off_dCp = take(bt * size_t(L) * size_t(pl.dtiles) * n * 4);
+  pl.grp = grouping(pl.Cf - 1);
+  pl.off_gS = take(bt * size_t(pl.grp.G) * d * 4);
+  pl.off_gB = take(bt * size_t(pl.grp.G) * d * n * 4);
   pl.total = off;
   return pl;
 }
@@ -477,7 +526,7 @@ ssm_status_t check_bwd(const ssm_scan_bwd_args_t* a, BwdPlan* plan) {
   const int64_t ng = ng_of(a->dstate);
   if (a->batch * plan->Cf * plan->dtiles > kMaxGrid ||
       a->batch * plan->Cs * plan->dtiles * ng > kMaxGrid || (bln + 255) / 256 > kMaxGrid ||
-      (bdn + 63) / 64 > kMaxGrid)
+      (bdn * std::max<int64_t>(1, plan->grp.G) + 63) / 64 > kMaxGrid)
     return fail(SSM_ERR_SHAPE, "problem too large for one launch");
   return SSM_OK;
 }
@@ -510,10 +559,9 @@ ssm_status_t run_bwd(const ssm_scan_bwd_args_t* a, const BwdPlan& pl, hipStream_
     fp.nwg = int32_t(a->batch * (pl.Cf - 1) * pl.dtiles);
     hipLaunchKernelGGL((k_chunk_summary<N, InT, DISC, false>), dim3(fp.nwg), dim3(kWave), 0, s, fp);
     if (ssm_status_t st = launch_status("k_chunk_summary (backward)")) return st;
-    const int64_t chains = a->batch * a->dim * N;
-    hipLaunchKernelGGL((k_carry_combine<N>), dim3(uint32_t((chains + 63) / 64)), dim3(kWave), 0, s,
-                       fp);
-    if (ssm_status_t st = launch_status("k_carry_combine (backward)")) return st;
+    fp.gS = reinterpret_cast<float*>(ws + pl.off_gS);
+    fp.gB = reinterpret_cast<float*>(ws + pl.off_gB);
+    if (ssm_status_t st = launch_combine<N>(fp, pl.grp, s)) return st;
   }
   BwdParams bp{};
   bp.x = a->x;
@@ -644,6 +692,11 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_args_t* a, void* hip_stream) {
   kp.conv_k = a->conv_w ? a->conv_k : 0;
   kp.dsum = pl.C > 1 ? static_cast<float*>(a->workspace) : nullptr;
   kp.hsum = pl.C > 1 ? reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pl.ws_dsum) : nullptr;
+  if (pl.grp.G > 0) {
+    char* wsb = static_cast<char*>(a->workspace);
+    kp.gS = reinterpret_cast<float*>(wsb + pl.ws_dsum + pl.ws_hsum);
+    kp.gB = reinterpret_cast<float*>(wsb + pl.ws_dsum + pl.ws_hsum + pl.ws_gS);
+  }
   kp.Bt = a->batch;
   kp.L = a->seqlen;
   kp.D = a->dim;

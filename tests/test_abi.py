@@ -3,6 +3,7 @@ include/ssm_scan.h, struct layout, status strings, the workspace/plan query,
 and every argument-error path (all of which return before any HIP call, so
 these run without a GPU; fake pointers are never dereferenced)."""
 import ctypes
+import math
 import os
 import re
 import subprocess
@@ -350,11 +351,22 @@ def plan(lib, **kw):
 
 
 def expected_ws(batch, L, D, N, T):
+    """dsum (Bt, C-1, D) and hsum (Bt, C-1, D, N) fp32, then -- when the
+    carry walk is grouped (more than 64 chunk summaries) -- the group sums
+    (Bt, G, D) and group states (Bt, G, D, N), G = ceil(sqrt(C - 1)) groups of
+    ceil((C - 1) / G) chunks; each buffer 256-byte aligned."""
     C = -(-L // T)
     if C <= 1:
         return 0
     al = lambda v: (v + 255) // 256 * 256
-    return al(batch * (C - 1) * D * 4) + al(batch * (C - 1) * D * N * 4)
+    ws = al(batch * (C - 1) * D * 4) + al(batch * (C - 1) * D * N * 4)
+    nc = C - 1
+    if nc > 64:
+        G = math.isqrt(nc - 1) + 1
+        gsz = -(-nc // G)
+        G = -(-nc // gsz)
+        ws += al(batch * G * D * 4) + al(batch * G * D * N * 4)
+    return ws
 
 
 @pytest.mark.parametrize("shape", [(2, 64, 32, 16), (8, 2048, 1536, 16), (4, 8192, 2560, 16),
