@@ -400,12 +400,15 @@ k_bwd_main(const BwdParams p) {
       for (int n = 0; n < NS; ++n) h[n] = h0c[n];
       float stash[H][NS];
       // x / Delta of K steps at a time, the next K requested before the
-      // current K are used (rows past the chunk: buffer loads return 0)
+      // current K are used.  Row offsets are clamped to the chunk's last row
+      // (the rows past it are never used; this keeps every access in bounds
+      // whether or not the descriptor's range check covers the SGPR offset).
+      auto roff = [&](int j) { return static_cast<uint32_t>(j < len ? j : len - 1) * row_in; };
       float xa[K], da[K];
 #pragma unroll
       for (int jj = 0; jj < K; ++jj) {
-        xa[jj] = ldb(rx, lo_in, jj * row_in, kIn);
-        da[jj] = ldb(rd, lo_in, jj * row_in, kIn);
+        xa[jj] = ldb(rx, lo_in, roff(jj), kIn);
+        da[jj] = ldb(rd, lo_in, roff(jj), kIn);
       }
 #pragma unroll
       for (int jb = 0; jb < (j0 + H) / K; ++jb) {
@@ -413,8 +416,8 @@ k_bwd_main(const BwdParams p) {
         const int nb = (jb + 1 < (j0 + H) / K) ? jb + 1 : jb;
 #pragma unroll
         for (int jj = 0; jj < K; ++jj) {
-          xn[jj] = ldb(rx, lo_in, (nb * K + jj) * row_in, kIn);
-          dn[jj] = ldb(rd, lo_in, (nb * K + jj) * row_in, kIn);
+          xn[jj] = ldb(rx, lo_in, roff(nb * K + jj), kIn);
+          dn[jj] = ldb(rd, lo_in, roff(nb * K + jj), kIn);
         }
         float Bb[K][NS];
 #pragma unroll
@@ -453,9 +456,10 @@ k_bwd_main(const BwdParams p) {
 #pragma unroll
       for (int jj = 0; jj < K; ++jj) {
         const int j = jb * K + jj;
-        ub[jj] = ldb(rx, lo_in, j * row_in, kIn);
-        db[jj] = ldb(rd, lo_in, j * row_in, kIn);
-        yb[jj] = ldb(ry, lo_in, j * row_in, kIn);
+        const uint32_t off = static_cast<uint32_t>(j < len ? j : len - 1) * row_in;
+        ub[jj] = ldb(rx, lo_in, off, kIn);
+        db[jj] = ldb(rd, lo_in, off, kIn);
+        yb[jj] = ldb(ry, lo_in, off, kIn);
         load_row<NS>(Bb[jj], Bc + (j < len ? j : len - 1) * N);
         load_row<NS>(Cb[jj], Cc + (j < len ? j : len - 1) * N);
       }

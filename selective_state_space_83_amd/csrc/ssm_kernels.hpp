@@ -447,7 +447,7 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
   const __amdgpu_buffer_rsrc_t ry =
       make_rsrc(static_cast<OutT*>(p.y) + (OUT ? chunk_base : 0),
                 OUT ? static_cast<uint32_t>(steps) * row_out : 0u);
-  uint32_t soff_in = 0, soff_out = 0;
+  uint32_t soff_out = 0;
   const InT* Brow = static_cast<const InT*>(p.Bm) + (b * p.L + t0) * N;
   const InT* Crow = static_cast<const InT*>(p.Cm) + (b * p.L + t0) * N;
 
@@ -510,26 +510,29 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
   const int32_t nblk = steps / kU;
   float xc[kU], dc[kU], zc[kU];
   constexpr InT* kIn = nullptr;
-  if (nblk > 0) {
+  // byte offset of row t of the chunk, clamped to its last row: rows past the
+  // chunk are loaded (so that every path issues the same loads) but never used
+  auto row_off = [&](int32_t t) {
+    return static_cast<uint32_t>(t < steps ? t : steps - 1) * row_in;
+  };
 #pragma unroll
-    for (int j = 0; j < kU; ++j) {
-      xc[j] = ldb(rx, lo_in, j * row_in, kIn);
-      dc[j] = ldb(rd, lo_in, j * row_in, kIn);
-      zc[j] = GATE ? ldb(rz, lo_in, j * row_in, kIn) : 0.0f;
-    }
+  for (int j = 0; j < kU; ++j) {
+    xc[j] = ldb(rx, lo_in, row_off(j), kIn);
+    dc[j] = ldb(rd, lo_in, row_off(j), kIn);
+    zc[j] = GATE ? ldb(rz, lo_in, row_off(j), kIn) : 0.0f;
   }
   for (int32_t blk = 0; blk < nblk; ++blk) {
-    // Prefetch the next block's x / Delta (/ z).  The loads are unconditional
-    // (the last block re-reads its own rows) so that the number of loads in
-    // flight is the same on every path and each wait covers only the older
-    // loads.
+    // Prefetch the next block's x / Delta (/ z) -- after the last block, the
+    // remainder's rows.  The loads are unconditional so that the number of
+    // loads in flight is the same on every path and each wait covers only
+    // the older loads.
     float xn[kU], dn[kU], zn[kU];
-    const uint32_t nsoff = soff_in + ((blk + 1 < nblk) ? kU * row_in : 0u);
+    const int32_t tn = (blk + 1) * kU;
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
-      xn[j] = ldb(rx, lo_in, nsoff + j * row_in, kIn);
-      dn[j] = ldb(rd, lo_in, nsoff + j * row_in, kIn);
-      zn[j] = GATE ? ldb(rz, lo_in, nsoff + j * row_in, kIn) : 0.0f;
+      xn[j] = ldb(rx, lo_in, row_off(tn + j), kIn);
+      dn[j] = ldb(rd, lo_in, row_off(tn + j), kIn);
+      zn[j] = GATE ? ldb(rz, lo_in, row_off(tn + j), kIn) : 0.0f;
     }
     // the block's step sizes from their pre-activations (wave-uniform branch)
     if (dtm != kDtRaw) {
@@ -548,24 +551,29 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
       for (int j = 1; j < kU; ++j) bs += dc[j];
       sum_add(bs);
     }
-    soff_in += kU * row_in;
 #pragma unroll
     for (int j = 0; j < kU; ++j) { xc[j] = xn[j]; dc[j] = dn[j]; zc[j] = zn[j]; }
   }
-  // remainder (fewer than kU steps); the current rows are in Bb0 / Cb0
-  for (int32_t t = nblk * kU; t < steps; ++t) {
-    const float xv = ldb(rx, lo_in, soff_in, kIn);
-    float dv = ldb(rd, lo_in, soff_in, kIn);
-    const float zv = GATE ? ldb(rz, lo_in, soff_in, kIn) : 0.0f;
-    if (dtm != kDtRaw) dv = dt_transform(dv, dtb, dtm);
-    one_step(xv, dv, zv, t + 1 < steps, Bb0, Bb1, Cb0, Cb1);
-    if constexpr (!OUT) sum_add(dv);
+  // remainder (fewer than kU steps) from the rows already in registers; the
+  // current B / C rows are in Bb0 / Cb0 (every block has an even step count)
+  const int32_t rem = steps - nblk * kU;
+  if (rem > 0) {
+    if (dtm != kDtRaw) {
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-      Bb0[n] = Bb1[n];
-      if constexpr (OUT) Cb0[n] = Cb1[n];
+      for (int j = 0; j < kU; ++j) dc[j] = dt_transform(dc[j], dtb, dtm);
     }
-    soff_in += row_in;
+    const int32_t tb = nblk * kU;
+#pragma unroll
+    for (int j = 0; j < kU; j += 2) {
+      if (j < rem) {
+        one_step(xc[j], dc[j], zc[j], tb + j + 1 < steps, Bb0, Bb1, Cb0, Cb1);
+        if constexpr (!OUT) sum_add(dc[j]);
+      }
+      if (j + 1 < rem) {
+        one_step(xc[j + 1], dc[j + 1], zc[j + 1], tb + j + 2 < steps, Bb1, Bb0, Cb1, Cb0);
+        if constexpr (!OUT) sum_add(dc[j + 1]);
+      }
+    }
   }
   if (!OUT && dsum_out) *dsum_out = dacc - dcomp;
   if constexpr (CONV && OUT) {
