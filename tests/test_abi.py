@@ -352,7 +352,8 @@ def plan(lib, **kw):
 
 def expected_ws(batch, L, D, N, T):
     """dsum (Bt, C-1, D) and hsum (Bt, C-1, D, N) fp32, then -- when the
-    carry walk is grouped (more than 64 chunk summaries) -- the group sums
+    carry walk is grouped (more than 64 chunk summaries and fewer than 65536
+    chains Bt * D * N) -- the group sums
     (Bt, G, D) and group states (Bt, G, D, N), G = ceil(sqrt(C - 1)) groups of
     ceil((C - 1) / G) chunks; each buffer 256-byte aligned."""
     C = -(-L // T)
@@ -361,7 +362,7 @@ def expected_ws(batch, L, D, N, T):
     al = lambda v: (v + 255) // 256 * 256
     ws = al(batch * (C - 1) * D * 4) + al(batch * (C - 1) * D * N * 4)
     nc = C - 1
-    if nc > 64:
+    if nc > 64 and batch * D * N < 65536:
         G = math.isqrt(nc - 1) + 1
         gsz = -(-nc // G)
         G = -(-nc // gsz)
