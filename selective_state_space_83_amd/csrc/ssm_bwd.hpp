@@ -38,6 +38,7 @@ namespace ssmk {
 constexpr int kBwdFine = 16;     // recompute chunk (steps held in registers)
 constexpr int kBwdBlock = 4;     // steps per LDS exchange
 constexpr int kBwdHalf = 8;      // steps whose states are held in registers at once
+constexpr int kRedPitch = kWave + 4;   // padded LDS row of the channel sums
 
 struct BwdParams {
   const void* x;
@@ -84,45 +85,67 @@ __device__ __forceinline__ bool any_exact(const ChanConst<NS, DISC>& cc, float d
 }
 
 // One backward step of one lane for its NS states: given dy, u, Delta and the
-// states before (hp) and after (hn) the step, accumulate the gradient terms
-// and move the adjoint g to the previous step.  EXACT carries the decay as
-// expm1 (slow decay); SERIES (some state of the wave has |z| < 1/16)
-// evaluates ZOH's factor f = expm1(z) / A and df/dA, for the states with
-// small |z| = |Delta A|, by their series:
+// states before (hp) and after (hn) the step, form the gradient terms of the
+// step (pB, pC per state; du and dDelta summed over the lane's states, both
+// overwritten), add the step's dA terms and move the adjoint g to the
+// previous step.  `exact` (wave-uniform) carries the decay as
+// G + expm1(Delta A) G for slow decay; only that product differs between the
+// two forms, so the rest of the step is shared code.  SERIES (some state of
+// the wave has |z| < 1/16) evaluates ZOH's factor f = expm1(z) / A and df/dA,
+// for the states with small |z| = |Delta A|, by their series:
 //   f = Delta (1 + z/2 + z^2/6 + z^3/24 + z^4/120),
 //   df/dA = Delta^2 (1/2 + z/3 + z^2/8 + z^3/30 + z^4/144),
 // which also give the A = 0 limits; (a - 1) / A and (Delta a - f) / A lose
-// relative precision there.  Both choices are wave-uniform.
-template <int NS, int DISC, bool EXACT, bool SERIES>
+// relative precision there.
+template <int NS, int DISC, bool SERIES>
 __device__ __forceinline__ void bwd_lane_step(float (&g)[NS], float (&dA)[NS],
                                               const ChanConst<NS, DISC>& cc, const float (&Av)[NS],
                                               const float (&Bv)[NS], const float (&Cv)[NS],
                                               const float (&hp)[NS], const float (&hn)[NS],
-                                              float u, float dv, float dyv,
+                                              float u, float dv, float dyv, bool exact,
                                               float (&pB)[NS], float (&pC)[NS], float& du,
                                               float& ddt) {
-  float gb = 0.0f;   // sum_n G B (Delta*B: du and dDelta's input term are Delta, u times it)
-  const float dvu = dv * u;
+  float z2[NS], a[NS], G[NS], ag[NS];
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
-    const float z2 = dv * cc.A2[n];
-    const float a = exp2_fast(z2);
-    const float G = fmaf(Cv[n], dyv, g[n]);
-    pC[n] = dyv * hn[n];
-    const float ag = EXACT ? fmaf(expm1_from(z2, a), G, G) : a * G;   // into h_{t-1}
-    const float agh = ag * hp[n];                     // shared by dDelta and dA
-    if constexpr (DISC == kDeltaB) {
-      pB[n] = G * dvu;
-      gb = fmaf(G, Bv[n], gb);
-      ddt = fmaf(Av[n], agh, ddt);
+    z2[n] = dv * cc.A2[n];
+    a[n] = exp2_fast(z2[n]);
+    G[n] = fmaf(Cv[n], dyv, g[n]);
+  }
+  if (exact) {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) ag[n] = fmaf(expm1_from(z2[n], a[n]), G[n], G[n]);
+  } else {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) ag[n] = a[n] * G[n];
+  }
+  if constexpr (DISC == kDeltaB) {
+    // du and dDelta's input term are Delta and u times sum_n G B
+    const float dvu = dv * u;
+    float gb = G[0] * Bv[0];
+    float dt = Av[0] * (ag[0] * hp[0]);
+    dA[0] = fmaf(dv, ag[0] * hp[0], dA[0]);
+#pragma unroll
+    for (int n = 1; n < NS; ++n) {
+      const float agh = ag[n] * hp[n];            // shared by dDelta and dA
+      gb = fmaf(G[n], Bv[n], gb);
+      dt = fmaf(Av[n], agh, dt);
       dA[n] = fmaf(dv, agh, dA[n]);
-    } else {
-      float f = (a - 1.0f) * cc.invA[n];
-      float dfda = fmaf(dv, a, -f) * cc.invA[n];
+    }
+#pragma unroll
+    for (int n = 0; n < NS; ++n) pB[n] = G[n] * dvu;
+    du = dv * gb;
+    ddt = fmaf(u, gb, dt);
+  } else {
+    float su = 0.0f, dt = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      float f = (a[n] - 1.0f) * cc.invA[n];
+      float dfda = fmaf(dv, a[n], -f) * cc.invA[n];
       if constexpr (SERIES) {
         // some state of the wave has |z| < 1/16: the series there, the direct
         // forms elsewhere (the series is truncated for small |z| only)
-        const float z = z2 * kLn2;
+        const float z = z2[n] * kLn2;
         float q1 = fmaf(z, 1.0f / 120.0f, 1.0f / 24.0f);
         q1 = fmaf(z, q1, 1.0f / 6.0f);
         q1 = fmaf(z, q1, 0.5f);
@@ -135,17 +158,20 @@ __device__ __forceinline__ void bwd_lane_step(float (&g)[NS], float (&dA)[NS],
         f = small ? dv * q1 : f;
         dfda = small ? (dv * dv) * q2 : dfda;
       }
+      const float agh = ag[n] * hp[n];
       const float Bu = Bv[n] * u;
-      pB[n] = G * (f * u);
-      du = fmaf(G * f, Bv[n], du);
-      ddt = fmaf(Av[n], agh, fmaf(ag, Bu, ddt));       // df/dDelta = a
-      dA[n] = fmaf(dv, agh, fmaf(G * dfda, Bu, dA[n]));
+      pB[n] = G[n] * (f * u);
+      su = fmaf(G[n] * f, Bv[n], su);
+      dt = fmaf(Av[n], agh, fmaf(ag[n], Bu, dt));       // df/dDelta = a
+      dA[n] = fmaf(dv, agh, fmaf(G[n] * dfda, Bu, dA[n]));
     }
-    g[n] = ag;
+    du = su;
+    ddt = dt;
   }
-  if constexpr (DISC == kDeltaB) {
-    du = fmaf(dv, gb, du);
-    ddt = fmaf(u, gb, ddt);
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    pC[n] = dyv * hn[n];
+    g[n] = ag[n];
   }
 }
 
@@ -293,10 +319,18 @@ k_bwd_main(const BwdParams p) {
   constexpr int NS = BwdLayout<N>::NS, NG = BwdLayout<N>::NG;
   constexpr int F = kBwdFine, K = kBwdBlock, H = kBwdHalf;
   static_assert(F % H == 0 && H % K == 0, "halves hold whole blocks");
-  // LDS: per wave the dB / dC products of one block, [kind][step][state][lane];
-  // per workgroup the du / dDelta partials, [kind][wave][step][lane]
-  __shared__ float red[NG][2][K][NS][kWave];
-  __shared__ float xch[2][NG][K][kWave];
+  // LDS.  Per wave, the dB / dC products of two steps as RR rows of 64
+  // channels, [step of the pair][kind][state]; each row is padded to
+  // kRedPitch floats, so the LPR lanes summing a row, reading 16 bytes each,
+  // touch 16 different bank groups.  The rows are private to the wave, so
+  // no workgroup barrier guards them.  Per workgroup, the du / dDelta
+  // partials of a block, [buffer][kind][wave][step][lane], double-buffered:
+  // one barrier per block separates their writes from their reads.
+  constexpr int RR = 4 * NS;           // rows summed together
+  constexpr int LPR = kWave / RR;      // lanes per row; each sums RR floats
+  static_assert(RR % 4 == 0 && LPR * RR == kWave && K % 2 == 0, "reduction layout");
+  __shared__ __attribute__((aligned(16))) float red[NG][RR][kRedPitch];
+  __shared__ float xch[2][2][NG][K][kWave];
 
   const int wg = xcd_remap(blockIdx.x, p.nwg);
   const int64_t dtile = wg % p.dtiles;
@@ -312,12 +346,9 @@ k_bwd_main(const BwdParams p) {
   const bool valid = dbase + lane < p.D;   // lanes past D duplicate D - 1 and add nothing
   if (!valid) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
-#pragma unroll
-      for (int jj = 0; jj < K; ++jj)
-#pragma unroll
-        for (int n = 0; n < NS; ++n) red[w][k][jj][n][lane] = 0.0f;
+    for (int rr = 0; rr < RR; ++rr) red[w][rr][lane] = 0.0f;
   }
+  int xb = 0;   // buffer of xch used by the current block (wave-uniform)
   const int n0 = w * NS;
 
   ChanConst<NS, DISC> cc;
@@ -394,7 +425,6 @@ k_bwd_main(const BwdParams p) {
     for (int half = F / H - 1; half >= 0; --half) {
       const int j0 = half * H;
       if (j0 >= len) continue;   // wave-uniform
-      const int hlen = (len - j0 < H) ? len - j0 : H;
       float h[NS];
 #pragma unroll
       for (int n = 0; n < NS; ++n) h[n] = h0c[n];
@@ -482,64 +512,67 @@ k_bwd_main(const BwdParams p) {
         const float (&Cv)[NS] = Cb[jj];
         if (j < len) {
           const int js = j - j0;                    // index within the half
-          const bool last = (js == hlen - 1);
+          // the state after step js: the stash holds the state before every
+          // step of the half, and past a short half's last step the state
+          // after it (the recompute stashes before it skips a step)
           float hn[NS];
 #pragma unroll
-          for (int n = 0; n < NS; ++n) hn[n] = last ? h[n] : stash[js + 1 < H ? js + 1 : js][n];
+          for (int n = 0; n < NS; ++n) hn[n] = (js + 1 < H) ? stash[js + 1 < H ? js + 1 : js][n] : h[n];
           // wave-uniform forms: slow decay, and (ZOH) small |Delta A| series
           const bool exact = any_exact<NS, DISC>(cc, dv);
           const bool series = DISC == kZoh && __builtin_amdgcn_ballot_w64(dv < zoh_thr) != 0;
-          if (exact) {
-            if (series)
-              bwd_lane_step<NS, DISC, true, true>(g, dAacc, cc, Av, Bv, Cv, stash[js], hn, u,
-                                                  dv, dyv, pB, pC, du, ddt);
-            else
-              bwd_lane_step<NS, DISC, true, false>(g, dAacc, cc, Av, Bv, Cv, stash[js], hn, u,
-                                                   dv, dyv, pB, pC, du, ddt);
-          } else {
-            if (series)
-              bwd_lane_step<NS, DISC, false, true>(g, dAacc, cc, Av, Bv, Cv, stash[js], hn, u,
-                                                   dv, dyv, pB, pC, du, ddt);
-            else
-              bwd_lane_step<NS, DISC, false, false>(g, dAacc, cc, Av, Bv, Cv, stash[js], hn, u,
-                                                    dv, dyv, pB, pC, du, ddt);
-          }
-          if (w == 0) dDacc = fmaf(dyv, u, dDacc);
+          if (series)
+            bwd_lane_step<NS, DISC, true>(g, dAacc, cc, Av, Bv, Cv, stash[js], hn, u, dv, dyv,
+                                          exact, pB, pC, du, ddt);
+          else
+            bwd_lane_step<NS, DISC, false>(g, dAacc, cc, Av, Bv, Cv, stash[js], hn, u, dv, dyv,
+                                           exact, pB, pC, du, ddt);
+          dDacc = fmaf(dyv, u, dDacc);   // every wave sums it; wave 0 stores it
         }
+        const int sp = jj & 1;   // the pair (jj | 1, jj & ~1) shares the rows
         if (valid) {   // lanes past the last channel keep their zero entries
 #pragma unroll
           for (int n = 0; n < NS; ++n) {
-            red[w][0][jj][n][lane] = pB[n];
-            red[w][1][jj][n][lane] = pC[n];
+            red[w][(sp * 2 + 0) * NS + n][lane] = pB[n];
+            red[w][(sp * 2 + 1) * NS + n][lane] = pC[n];
           }
         }
-        xch[0][w][jj][lane] = du;
-        xch[1][w][jj][lane] = ddt;
+        xch[xb][0][w][jj][lane] = du;
+        xch[xb][1][w][jj][lane] = ddt;
+        if (sp == 0) {
+          // dB / dC of steps jj + 1 and jj: LPR lanes sum each row over the
+          // wave's 64 channels (the wave's own LDS writes are seen in order)
+          __builtin_amdgcn_wave_barrier();
+          const int rr = lane / LPR, c = lane % LPR;
+          const float4* src = reinterpret_cast<const float4*>(&red[w][rr][c * RR]);
+          float acc = 0.0f;
+#pragma unroll
+          for (int i = 0; i < RR / 4; ++i) {
+            const float4 v = src[i];
+            acc += v.x;
+            acc += v.y;
+            acc += v.z;
+            acc += v.w;
+          }
+          if constexpr (LPR >= 2)   // quad_perm [1, 0, 3, 2]
+            acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xF, 0xF, false));
+          if constexpr (LPR >= 4)   // quad_perm [2, 3, 0, 1]
+            acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xF, 0xF, false));
+          if constexpr (LPR >= 8)   // row_half_mirror
+            acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x141, 0xF, 0xF, false));
+          if constexpr (LPR >= 16)  // row_mirror
+            acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x140, 0xF, 0xF, false));
+          const int jr = jj + rr / (2 * NS);
+          const int kind = (rr / NS) & 1;
+          const int n = rr % NS;
+          if (c == 0 && jb * K + jr < len) {
+            float* dst = kind == 0 ? p.dBp : p.dCp;
+            dst[((b * p.L + t0 + jb * K + jr) * p.dtiles + dtile) * N + n0 + n] = acc;
+          }
+          __builtin_amdgcn_wave_barrier();   // the reads stay ahead of the next pair's writes
+        }
       }
       __syncthreads();
-      // dB / dC: each pair of lanes sums one (kind, step, state) over the
-      // wave's 64 channels
-      {
-        constexpr int Q = 2 * K * NS;   // sums per wave (at most 32)
-        const int q = lane >> 1, half = lane & 1;
-        float acc = 0.0f;
-        if (q < Q) {
-          const float* src = &red[w][0][0][0][0] + q * kWave + half * (kWave / 2);
-#pragma unroll
-          for (int i = 0; i < kWave / 2; ++i) acc += src[i];
-        }
-        acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xF, 0xF, false));
-        if (q < Q && half == 0) {
-          const int kind = q / (K * NS);
-          const int jj = (q % (K * NS)) / NS;
-          const int n = q % NS;
-          const int j = jb * K + jj;
-          if (j < len) {
-            float* dst = kind == 0 ? p.dBp : p.dCp;
-            dst[((b * p.L + t0 + j) * p.dtiles + dtile) * N + n0 + n] = acc;
-          }
-        }
-      }
       // du / dDelta: wave w finishes steps jj = w, w + NG, ...
 #pragma unroll
       for (int jj = w; jj < K; jj += NG) {
@@ -548,15 +581,15 @@ k_bwd_main(const BwdParams p) {
           float su = 0.0f, sd = 0.0f;
 #pragma unroll
           for (int v = 0; v < NG; ++v) {
-            su += xch[0][v][jj][lane];
-            sd += xch[1][v][jj][lane];
+            su += xch[xb][0][v][jj][lane];
+            sd += xch[xb][1][v][jj][lane];
           }
           const float dyv = ldb(ry, lo_in, j * row_in, kIn);
           stb(rdx, lo_f, j * row_f, fmaf(dsk, dyv, su), kF);
           stb(rdd, lo_f, j * row_f, sd, kF);
         }
       }
-      __syncthreads();
+      xb ^= 1;   // the next block's exchange goes to the other buffer
     }
     }
   }
