@@ -27,7 +27,11 @@ The reported bound is the roof with the higher utilisation.
 scan for upstream gradients dy ~ N(0, 1) and dh_last ~ N(0, 1); the roofline
 entry is that of the main backward kernel k_bwd_main (VALU lane-slots per
 element: 20 for Delta*B, 28 for ZOH -- the forward recompute plus the
-adjoint step, its four gradient products and the channel-sum adds).
+adjoint step, its four gradient products and the channel-sum adds).  The
+backward starts from the states the forward scan kept every 16 steps
+(h_saved, written by one forward call before the timed region, as in
+training); --recompute-states times the backward that computes them itself.
+--train times forward (keeping the states) plus backward as one step.
 
 --fused runs the same workload with every fused step on: the step size from
 its pre-activation (softplus(delta + bias[d])), the gate y * silu(z) and, with
@@ -273,7 +277,9 @@ def bench_decode(w, steps, warmup, torch, ssm, fused=False):
     return dict(total_ms=e0.elapsed_time(e1), wall_s=wall, launch_us=launch_us)
 
 
-def bench_bwd(w, steps, warmup, torch, ssm):
+def bench_bwd(w, steps, warmup, torch, ssm, kept=True, train=False):
+    """Backward (train=False) or forward + backward (train=True) steps; with
+    kept=True the backward starts from the forward's kept states."""
     import ssm_inputs as SI
     inp = SI.scan_inputs(w, h0=True)
     gi = SI.grad_inputs(w)
@@ -281,18 +287,30 @@ def bench_bwd(w, steps, warmup, torch, ssm):
     A, Dv, h0 = (to_dev(inp[k], "f32", torch) for k in ("A", "D", "h0"))
     dy = to_dev(gi["dy"], w.in_dtype, torch)
     dhl = to_dev(gi["dh_last"], "f32", torch)
+    hs = None
+    if kept or train:
+        hs = torch.empty(ssm.saved_states_shape(w.batch, w.seqlen, w.dim, w.dstate),
+                         dtype=torch.float32, device="cuda")
+    fwd, _, _ = ssm.prepare_scan(t["x"], t["delta"], A, t["B"], t["C"], Dv, h0=h0, zoh=w.zoh,
+                                 h_saved=hs)
     prep, _ = ssm.prepare_bwd(t["x"], t["delta"], A, t["B"], t["C"], dy, D=Dv, h0=h0,
-                              dh_last=dhl, zoh=w.zoh)
+                              dh_last=dhl, zoh=w.zoh, h_saved=hs)
     hip = HipEvents()
     evs = hip.create(2 * steps)
     stream = torch.cuda.current_stream()
+    if hs is not None:
+        fwd.run(stream)          # the states the backward starts from
     for _ in range(warmup):
+        if train:
+            fwd.run(stream)
         prep.run(stream)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(steps):
+        if train:
+            fwd.run(stream)
         prep.run(stream, events=(evs[2 * i], evs[2 * i + 1]))
     e1.record(stream)
     torch.cuda.synchronize()
@@ -339,6 +357,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward scan (ssm_scan_bwd) of the workload")
+    ap.add_argument("--recompute-states", action="store_true",
+                    help="with --backward: the backward computes the forward states itself")
+    ap.add_argument("--train", action="store_true",
+                    help="time forward (keeping the states) + backward as one step")
     ap.add_argument("--fused", action="store_true",
                     help="run with the fused steps on (softplus step size, gate, conv window)")
     ap.add_argument("--chunk-len", type=int, default=0,
@@ -401,8 +423,9 @@ def main():
         print(json.dumps(out), flush=True)
         return
 
-    if args.backward:
-        r = bench_bwd(w, args.steps, args.warmup, torch, ssm)
+    if args.backward or args.train:
+        kept = not args.recompute_states
+        r = bench_bwd(w, args.steps, args.warmup, torch, ssm, kept=kept, train=args.train)
         ms = r["total_ms"] / args.steps
         main_us = float(np.mean(r["main_ms"])) * 1e3
         slots = w.elems * SLOTS_BWD_ELEM[w.zoh]
@@ -414,7 +437,11 @@ def main():
                "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
                "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
                "dtype": "f32", "data": "synthetic",
-               "config": {"workload": w.name, "pass": "backward", "batch": w.batch,
+               "config": {"workload": w.name,
+                          "pass": "forward+backward" if args.train else "backward",
+                          "states": "kept by the forward" if (kept or args.train)
+                          else "recomputed",
+                          "batch": w.batch,
                           "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
                           "in_dtype": w.in_dtype, "disc": "zoh" if w.zoh else "delta_b"},
                "roofline": roof, "cpu_baseline": None}

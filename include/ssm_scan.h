@@ -92,7 +92,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 typedef enum {
   SSM_OK = 0,
@@ -101,7 +101,9 @@ typedef enum {
   SSM_ERR_DTYPE = 3,       /* unknown dtype or discretization enum value */
   SSM_ERR_UNSUPPORTED = 4, /* dstate not in {1,2,4,8,16}, conv_k not in 1..4,
                               misaligned pointer, negative chunk_len, reserved != 0,
-                              delta_softplus not 0/1, conv state without conv_w */
+                              delta_softplus not 0/1, conv state without conv_w,
+                              h_saved with a split scan whose chunk_len is not a
+                              multiple of 4 */
   SSM_ERR_ALIAS = 5,       /* an output overlaps an input or another output */
   SSM_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
   SSM_ERR_HIP = 7          /* the HIP runtime rejected a launch */
@@ -143,6 +145,13 @@ typedef struct {
                                          requires conv_w */
   float* conv_state_out;              /* (Bt, D, K-1) receives the last K-1 inputs, or NULL;
                                          requires conv_w; must not overlap any other buffer */
+  /* since ABI 3 */
+  float* h_saved;                     /* (Bt, S, D, N) fp32 or NULL, S = ceil(L / 16) - 1:
+                                         receives the state entering steps 16, 32, ..., 16 S
+                                         (h_saved[b][k-1] = h before step 16 k), for
+                                         ssm_scan_bwd; must not overlap any other buffer.
+                                         When the scan is split into chunks, their length
+                                         must be a multiple of 4 (the planned length is) */
 } ssm_scan_args_t;
 
 typedef struct {
@@ -182,8 +191,11 @@ typedef struct {
  *   dx_t = sum_n g_t f_t B_t + Dskip dy_t, dDelta_t, dA, dB, dC, dD, dh0.
  * All gradients are fp32 and overwritten (not accumulated).  Inputs are as
  * in ssm_scan_args_t; dy has in_dtype.  The adjoint is chunked like the
- * forward scan and the forward states are recomputed, so nothing of size
- * batch x L x D x N is stored. */
+ * forward scan and the forward states are recomputed between states kept
+ * every 16 steps, so nothing of size batch x L x D x N is stored.  The
+ * states every 16 steps are either computed here (a forward summary and
+ * carry pass) or taken from the forward scan of the same inputs (h_saved of
+ * ssm_scan_args_t), which skips that pass. */
 typedef struct {
   int64_t batch, seqlen, dim, dstate; /* Bt, L, D, N */
   int32_t in_dtype;                   /* ssm_dtype_t of x, delta, Bm, Cm, dy */
@@ -210,6 +222,10 @@ typedef struct {
   size_t workspace_bytes;
   void* ev_main_start;                /* optional hipEvent_t recorded on hip_stream right */
   void* ev_main_stop;                 /* before / after the main backward kernel; NULL = none */
+  /* since ABI 3 */
+  const float* h_saved;               /* (Bt, ceil(L / 16) - 1, D, N) or NULL: the states
+                                         ssm_scan_fwd wrote to its h_saved for the same x,
+                                         delta, A, Bm, h0 (and disc); NULL = computed here */
 } ssm_scan_bwd_args_t;
 
 /* Returns SSM_ABI_VERSION. */
@@ -240,7 +256,8 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_args_t* args, void* hip_stream);
 ssm_status_t ssm_step(const ssm_step_args_t* args, void* hip_stream);
 
 /* Bytes of device workspace ssm_scan_bwd needs (never 0 for a non-empty
- * problem).  Pure host function; 0 for invalid sizes. */
+ * problem; smaller when h_saved is given).  Pure host function; 0 for
+ * invalid sizes. */
 size_t ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args_t* args);
 
 /* Backward selective scan (see ssm_scan_bwd_args_t).  Asynchronous on

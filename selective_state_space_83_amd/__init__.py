@@ -38,6 +38,13 @@ SSM_ERR_ALIAS = 5
 SSM_ERR_WORKSPACE = 6
 SSM_ERR_HIP = 7
 
+# the version of include/ssm_scan.h these structures mirror; load_library
+# refuses a library built from another one (its structs would differ)
+ABI_VERSION = 3
+
+# states kept for the backward pass: one every SAVE_STRIDE steps
+SAVE_STRIDE = 16
+
 SSM_F32 = 0
 SSM_BF16 = 1
 SSM_DISC_DELTA_B = 0
@@ -61,6 +68,7 @@ class ScanArgs(ctypes.Structure):
         ("delta_bias", ctypes.c_void_p), ("delta_softplus", ctypes.c_int32),
         ("reserved2", ctypes.c_int32), ("z", ctypes.c_void_p),
         ("conv_state_in", ctypes.c_void_p), ("conv_state_out", ctypes.c_void_p),
+        ("h_saved", ctypes.c_void_p),
     ]
 
 
@@ -94,6 +102,7 @@ class BwdArgs(ctypes.Structure):
         ("dh0", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("ev_main_start", ctypes.c_void_p), ("ev_main_stop", ctypes.c_void_p),
+        ("h_saved", ctypes.c_void_p),
     ]
 
 
@@ -131,6 +140,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssm_status_string.argtypes = [ctypes.c_int]
     lib.ssm_last_error_message.restype = ctypes.c_char_p
     lib.ssm_last_error_message.argtypes = []
+    got = int(lib.ssm_abi_version())
+    if got != ABI_VERSION:
+        raise RuntimeError("%s has ABI version %d, this binding mirrors version %d; rebuild it"
+                           % (path, got, ABI_VERSION))
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -196,9 +209,16 @@ def _stream_handle(stream) -> Optional[int]:
     return s.cuda_stream
 
 
+def saved_states_shape(batch: int, seqlen: int, dim: int, dstate: int) -> tuple:
+    """Shape of the states a scan keeps for the backward pass (h_saved): the
+    state entering steps 16, 32, ... below seqlen."""
+    n = (seqlen + SAVE_STRIDE - 1) // SAVE_STRIDE - 1 if seqlen > 0 else 0
+    return (batch, n, dim, dstate)
+
+
 def make_scan_args(x, delta, A, B, C, D=None, h0=None, h_last=None, y=None, conv_w=None,
                    conv_b=None, zoh=False, chunk_len=0, delta_bias=None, delta_softplus=False,
-                   z=None, conv_state_in=None, conv_state_out=None) -> ScanArgs:
+                   z=None, conv_state_in=None, conv_state_out=None, h_saved=None) -> ScanArgs:
     """Fill a ScanArgs from tensors (shape checks are the library's job)."""
     if x.dim() != 3 or A.dim() != 2:
         raise ValueError("x must be (batch, L, dim) and A (dim, N)")
@@ -242,7 +262,17 @@ def make_scan_args(x, delta, A, B, C, D=None, h0=None, h_last=None, y=None, conv
     a.conv_state_out = _ptr(_f32(conv_state_out, "conv_state_out"))
     _fill_fused(a, dim, delta_bias, delta_softplus, z, tuple(x.shape))
     a.chunk_len = int(chunk_len)
+    a.h_saved = _saved_ptr(h_saved, batch, L, dim, a.dstate)
     return a
+
+
+def _saved_ptr(h_saved, batch, L, dim, N):
+    if h_saved is None:
+        return None
+    want = saved_states_shape(batch, L, dim, N)
+    if tuple(h_saved.shape) != want:
+        raise ValueError("h_saved must be %s" % (want,))
+    return _ptr(_f32(h_saved, "h_saved"))
 
 
 def _fill_fused(a, dim, delta_bias, delta_softplus, z, z_shape):
@@ -273,14 +303,17 @@ def abi_version() -> int:
 def scan(x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None, zoh=False,
          out_dtype=None, want_h_last=True, y=None, h_last=None, chunk_len=0,
          workspace=None, stream=None, events=None, delta_bias=None, delta_softplus=False,
-         z=None, conv_state_in=None, conv_state_out=None) -> Tuple[object, object]:
+         z=None, conv_state_in=None, conv_state_out=None,
+         h_saved=None) -> Tuple[object, object]:
     """Selective-scan forward on the current (or given) stream.
 
     Returns (y, h_last); h_last is None when want_h_last is False and no
     h_last tensor is passed.  ``workspace`` (uint8 device tensor) may be
     passed to avoid an allocation per call; ``events`` = (start, stop) raw
     hipEvent_t handles recorded around the output-pass kernel.
-    ``conv_state_out`` (float32 (batch, dim, K - 1)) is filled in place."""
+    ``conv_state_out`` (float32 (batch, dim, K - 1)) is filled in place, and
+    so is ``h_saved`` (float32, ``saved_states_shape(...)``), the states the
+    backward pass (``scan_bwd(..., h_saved=...)``) starts from."""
     torch = _torch()
     lib = load_library()
     if y is None:
@@ -290,7 +323,7 @@ def scan(x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None, zoh=False
         h_last = torch.empty((x.shape[0], x.shape[2], A.shape[1]), dtype=torch.float32,
                              device=x.device)
     args = make_scan_args(x, delta, A, B, C, D, h0, h_last, y, conv_w, conv_b, zoh, chunk_len,
-                          delta_bias, delta_softplus, z, conv_state_in, conv_state_out)
+                          delta_bias, delta_softplus, z, conv_state_in, conv_state_out, h_saved)
     need = int(lib.ssm_scan_workspace_size(ctypes.byref(args)))
     if need > 0:
         if workspace is None or workspace.numel() < need:
@@ -327,7 +360,7 @@ class PreparedScan:
 def prepare_scan(x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None, zoh=False,
                  y=None, h_last=None, chunk_len=0, workspace=None, out_dtype=None,
                  delta_bias=None, delta_softplus=False, z=None, conv_state_in=None,
-                 conv_state_out=None):
+                 conv_state_out=None, h_saved=None):
     """Allocate outputs and workspace (if not given), check and marshal the
     arguments once; returns (PreparedScan, y, h_last)."""
     torch = _torch()
@@ -336,7 +369,7 @@ def prepare_scan(x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None, z
         y = torch.empty(x.shape, dtype=out_dtype if out_dtype is not None else x.dtype,
                         device=x.device)
     args = make_scan_args(x, delta, A, B, C, D, h0, h_last, y, conv_w, conv_b, zoh, chunk_len,
-                          delta_bias, delta_softplus, z, conv_state_in, conv_state_out)
+                          delta_bias, delta_softplus, z, conv_state_in, conv_state_out, h_saved)
     need = int(lib.ssm_scan_workspace_size(ctypes.byref(args)))
     if need > 0 and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -344,7 +377,7 @@ def prepare_scan(x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None, z
         args.workspace = _ptr(workspace)
         args.workspace_bytes = workspace.numel()
     keep = (x, delta, A, B, C, D, h0, h_last, y, conv_w, conv_b, workspace, delta_bias, z,
-            conv_state_in, conv_state_out)
+            conv_state_in, conv_state_out, h_saved)
     return PreparedScan(args, keep), y, h_last
 
 
@@ -437,9 +470,10 @@ def step(h, x, delta, A, B, C, D=None, zoh=False, y=None, out_dtype=None, stream
 
 
 def make_bwd_args(x, delta, A, B, C, dy, D=None, h0=None, dh_last=None, zoh=False, grads=None,
-                  super_chunk=0) -> BwdArgs:
+                  super_chunk=0, h_saved=None) -> BwdArgs:
     """Fill a BwdArgs; ``grads`` is the dict of float32 gradient tensors
-    (dx, ddelta, dA, dB, dC and optionally dD, dh0)."""
+    (dx, ddelta, dA, dB, dC and optionally dD, dh0); ``h_saved`` the states
+    kept by the forward scan of the same inputs, or None."""
     if x.dim() != 3 or A.dim() != 2:
         raise ValueError("x must be (batch, L, dim) and A (dim, N)")
     batch, L, dim = x.shape
@@ -472,6 +506,7 @@ def make_bwd_args(x, delta, A, B, C, dy, D=None, h0=None, dh_last=None, zoh=Fals
     a.h0 = _ptr(_f32(h0, "h0"))
     a.dy = _ptr(dy)
     a.dh_last = _ptr(_f32(dh_last, "dh_last"))
+    a.h_saved = _saved_ptr(h_saved, batch, L, dim, N)
     return a
 
 
@@ -509,25 +544,25 @@ def _bwd_outputs(x, A, want_dD, want_dh0):
 
 
 def prepare_bwd(x, delta, A, B, C, dy, D=None, h0=None, dh_last=None, zoh=False,
-                want_dD=True, want_dh0=True, super_chunk=0, workspace=None):
+                want_dD=True, want_dh0=True, super_chunk=0, workspace=None, h_saved=None):
     """Allocate the gradients and the workspace, check and marshal once;
     returns (PreparedBwd, grads dict)."""
     torch = _torch()
     lib = load_library()
     g = _bwd_outputs(x, A, want_dD, want_dh0)
-    args = make_bwd_args(x, delta, A, B, C, dy, D, h0, dh_last, zoh, g, super_chunk)
+    args = make_bwd_args(x, delta, A, B, C, dy, D, h0, dh_last, zoh, g, super_chunk, h_saved)
     need = int(lib.ssm_scan_bwd_workspace_size(ctypes.byref(args)))
     if need > 0 and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     if need > 0:
         args.workspace = _ptr(workspace)
         args.workspace_bytes = workspace.numel()
-    keep = (x, delta, A, B, C, dy, D, h0, dh_last, workspace) + tuple(g.values())
+    keep = (x, delta, A, B, C, dy, D, h0, dh_last, workspace, h_saved) + tuple(g.values())
     return PreparedBwd(args, keep), {k: v for k, v in g.items() if v is not None}
 
 
 def scan_bwd(x, delta, A, B, C, dy, D=None, h0=None, dh_last=None, zoh=False, want_dD=True,
-             want_dh0=True, super_chunk=0, workspace=None, stream=None) -> dict:
+             want_dh0=True, super_chunk=0, workspace=None, stream=None, h_saved=None) -> dict:
     """Backward selective scan on the current (or given) stream: the
     gradients of sum(dy * y) + sum(dh_last * h_last) of ``scan`` (no fused
     steps).  Returns a dict of float32 tensors dx, ddelta, dA, dB, dC and,
@@ -536,7 +571,7 @@ def scan_bwd(x, delta, A, B, C, dy, D=None, h0=None, dh_last=None, zoh=False, wa
     lib = load_library()
     dev = x.device
     g = _bwd_outputs(x, A, want_dD, want_dh0)
-    args = make_bwd_args(x, delta, A, B, C, dy, D, h0, dh_last, zoh, g, super_chunk)
+    args = make_bwd_args(x, delta, A, B, C, dy, D, h0, dh_last, zoh, g, super_chunk, h_saved)
     need = int(lib.ssm_scan_bwd_workspace_size(ctypes.byref(args)))
     if need > 0:
         if workspace is None or workspace.numel() < need:

@@ -39,6 +39,7 @@ constexpr int kBwdFine = 16;     // recompute chunk (steps held in registers)
 constexpr int kBwdBlock = 4;     // steps per LDS exchange
 constexpr int kBwdHalf = 8;      // steps whose states are held in registers at once
 constexpr int kRedPitch = kWave + 4;   // padded LDS row of the channel sums
+static_assert(kBwdFine == kSaveStride, "the forward keeps the states the backward starts from");
 
 struct BwdParams {
   const void* x;

@@ -91,7 +91,14 @@ struct ScanParams {
   float* gS;             // (Bt, G, D)     group sums of Delta
   float* gB;             // (Bt, G, D, N)  group end states from zero, then carries into groups
   int64_t G, gsz;
+  // states kept for the backward pass: the state entering every
+  // kSaveStride-th step, (Bt, nsave, D, N), or null
+  float* hsave;
+  int64_t nsave;
 };
+
+// Steps between the states the output pass keeps for the backward pass.
+constexpr int kSaveStride = 16;
 
 // How the step size is formed from the given delta values.
 enum DtMode : int { kDtRaw = 0, kDtBias = 1, kDtSoftplus = 2 };
@@ -361,6 +368,7 @@ __device__ __forceinline__ Tile tile_of(int wg, int64_t dtiles, int64_t nchunks)
 // ahead): the summary pass does less arithmetic per step, so it looks
 // further ahead to cover the same memory latency.
 constexpr int kUnrollOut = 4;
+static_assert(kSaveStride % kUnrollOut == 0, "kept states fall on block ends");
 #ifndef SSM_UNROLL_SUM
 #define SSM_UNROLL_SUM 8
 #endif
@@ -410,13 +418,16 @@ __device__ __forceinline__ void stb(__amdgpu_buffer_rsrc_t r, uint32_t voff, uin
 // step, after the loads had a full step to land.)
 //
 // GATE (output pass only) streams z like x and multiplies each output by
-// silu(z).  cs_save, when not null, receives the conv window after the last
+// silu(z).  SAVE (output pass only) writes the state entering every
+// kSaveStride-th step to p.hsave.  cs_save, when not null, receives the conv window after the last
 // step (the caller passes it for the final chunk only).
-template <int N, typename InT, typename OutT, int DISC, bool CONV, bool OUT, bool GATE>
+template <int N, typename InT, typename OutT, int DISC, bool CONV, bool OUT, bool GATE,
+          bool SAVE = false>
 __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64_t dbase,
                                            uint32_t lo, int64_t t0, int32_t steps, float (&h)[N],
                                            float* dsum_out, float* cs_save) {
   static_assert(OUT || !GATE, "the gate applies to the output pass");
+  static_assert(OUT || !SAVE, "the output pass keeps the states");
   // (the conv prologue's extra registers would push an 8-step summary block
   // past 128 VGPRs, so conv summaries prefetch 6 steps ahead)
   constexpr int kU = OUT ? kUnrollOut : (CONV ? 6 : kUnrollSum);
@@ -544,6 +555,17 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
     for (int j = 0; j < kU; j += 2) {
       one_step(xc[j], dc[j], zc[j], tb + j + 1 < steps, Bb0, Bb1, Cb0, Cb1);
       one_step(xc[j + 1], dc[j + 1], zc[j + 1], tb + j + 2 < steps, Bb1, Bb0, Cb1, Cb0);
+    }
+    if constexpr (SAVE) {
+      // keep the state entering step te when te is a multiple of kSaveStride
+      // (chunks start on multiples of kU, so such steps end a block; the
+      // remainder after the last block holds none below L)
+      const int64_t te = t0 + tb + kU;
+      if (te % kSaveStride == 0 && te < p.L) {
+        float* dst = p.hsave + ((b * p.nsave + te / kSaveStride - 1) * D + d) * N;
+#pragma unroll
+        for (int n = 0; n < N; ++n) dst[n] = h[n];
+      }
     }
     if constexpr (!OUT) {
       float bs = dc[0];
@@ -750,7 +772,7 @@ __global__ void __launch_bounds__(kWave) k_combine_apply(const ScanParams p) {
 
 // Pass 3 (or the only pass): scan each chunk from its carry-in, write y, and
 // h_last from the final chunk.
-template <int N, typename InT, typename OutT, int DISC, bool CONV, bool GATE>
+template <int N, typename InT, typename OutT, int DISC, bool CONV, bool GATE, bool SAVE>
 __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(4)))
 k_scan_out(const ScanParams p) {
   const int wg = xcd_remap(blockIdx.x, p.nwg);
@@ -779,8 +801,8 @@ k_scan_out(const ScanParams p) {
   float* cs_save = (CONV && last && p.cs_out && p.conv_k > 1)
                        ? p.cs_out + (tl.b * p.D + d) * (p.conv_k - 1)
                        : nullptr;
-  chunk_loop<N, InT, OutT, DISC, CONV, true, GATE>(p, tl.b, dbase, lo, t0, steps, h, nullptr,
-                                                   cs_save);
+  chunk_loop<N, InT, OutT, DISC, CONV, true, GATE, SAVE>(p, tl.b, dbase, lo, t0, steps, h,
+                                                         nullptr, cs_save);
   if (p.h_last && last) {
     float* hl = p.h_last + (tl.b * p.D + d) * N;
 #pragma unroll

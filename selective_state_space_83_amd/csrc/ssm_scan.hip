@@ -48,6 +48,11 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 bool supported_n(int64_t n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; }
 
+// States kept for the backward pass: those entering steps 16, 32, ... < L.
+int64_t saved_count(int64_t L) {
+  return L > 0 ? (L + ssmk::kSaveStride - 1) / ssmk::kSaveStride - 1 : 0;
+}
+
 // A carry walk over more than kGroupWalk chunks is done in groups (three
 // parallel steps instead of one sequential chain per (b, d, n)) when it has
 // fewer than kGroupChains chains.  With that many chains the sequential walk
@@ -166,6 +171,14 @@ ssm_status_t check_scan(const ssm_scan_args_t* a, Plan* plan) {
   const Range csi{win > 0 ? a->conv_state_in : nullptr, size_t(bds) * 4};
   if (misaligned(a->conv_state_in, 4) || misaligned(a->conv_state_out, 4))
     return fail(SSM_ERR_UNSUPPORTED, "misaligned conv state (4 bytes)");
+  // kept states: the output pass writes them at block ends, which fall on
+  // multiples of 16 only when chunks start on multiples of 4
+  const int64_t nsave = saved_count(a->seqlen);
+  const Range hsv{nsave > 0 ? a->h_saved : nullptr, size_t(bdn) * size_t(nsave) * 4};
+  if (misaligned(a->h_saved, 4)) return fail(SSM_ERR_UNSUPPORTED, "misaligned h_saved (4 bytes)");
+  if (hsv.p && plan->C > 1 && plan->T % ssmk::kUnrollOut != 0)
+    return fail(SSM_ERR_UNSUPPORTED, "h_saved needs a chunk length that is a multiple of %d "
+                "(got %lld)", ssmk::kUnrollOut, (long long)plan->T);
   if (a->seqlen == 0 || a->batch * a->dim == 0) {
     // only h_last (with h0 or zeros) and conv_state_out (with conv_state_in or
     // zeros) may be written
@@ -202,10 +215,13 @@ ssm_status_t check_scan(const ssm_scan_args_t* a, Plan* plan) {
     if (overlap(y, r)) return fail(SSM_ERR_ALIAS, "y overlaps an input");
     if (overlap(hl, r)) return fail(SSM_ERR_ALIAS, "h_last overlaps an input");
     if (overlap(cso, r)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps an input");
+    if (overlap(hsv, r)) return fail(SSM_ERR_ALIAS, "h_saved overlaps an input");
   }
   if (overlap(y, hl)) return fail(SSM_ERR_ALIAS, "y overlaps h_last");
   if (overlap(y, cso) || overlap(hl, cso))
     return fail(SSM_ERR_ALIAS, "conv_state_out overlaps an output");
+  if (overlap(hsv, y) || overlap(hsv, hl) || overlap(hsv, cso))
+    return fail(SSM_ERR_ALIAS, "h_saved overlaps an output");
   if (plan->ws_total > 0) {
     if (!a->workspace) return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required", plan->ws_total);
     if (a->workspace_bytes < plan->ws_total)
@@ -214,7 +230,7 @@ ssm_status_t check_scan(const ssm_scan_args_t* a, Plan* plan) {
     const Range ws{a->workspace, plan->ws_total};
     for (const Range& r : ins)
       if (overlap(ws, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps an input");
-    if (overlap(ws, y) || overlap(ws, hl) || overlap(ws, cso))
+    if (overlap(ws, y) || overlap(ws, hl) || overlap(ws, cso) || overlap(ws, hsv))
       return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
   }
   const int64_t grid_out = a->batch * plan->C * plan->dtiles;
@@ -334,8 +350,12 @@ ssm_status_t run_scan(ssmk::ScanParams kp, const Plan& pl, hipStream_t s, hipEve
   }
   kp.nwg = int32_t(kp.Bt * pl.C * pl.dtiles);
   if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return fail(SSM_ERR_HIP, "hipEventRecord failed");
-  hipLaunchKernelGGL((ssmk::k_scan_out<N, InT, OutT, DISC, CONV, GATE>), dim3(kp.nwg),
-                     dim3(ssmk::kWave), 0, s, kp);
+  if (kp.hsave)
+    hipLaunchKernelGGL((ssmk::k_scan_out<N, InT, OutT, DISC, CONV, GATE, true>), dim3(kp.nwg),
+                       dim3(ssmk::kWave), 0, s, kp);
+  else
+    hipLaunchKernelGGL((ssmk::k_scan_out<N, InT, OutT, DISC, CONV, GATE, false>), dim3(kp.nwg),
+                       dim3(ssmk::kWave), 0, s, kp);
   if (ssm_status_t st = launch_status("k_scan_out")) return st;
   if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return fail(SSM_ERR_HIP, "hipEventRecord failed");
   return SSM_OK;
@@ -421,7 +441,8 @@ struct BwdPlan {
 int ng_of(int64_t N) { return N < 4 ? 1 : int(N / 4); }
 
 // Sizes assumed validated.
-BwdPlan make_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t super_chunk) {
+BwdPlan make_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t super_chunk,
+                      bool saved) {
   BwdPlan pl;
   const int64_t F = ssmk::kBwdFine;
   pl.dtiles = (D + ssmk::kWave - 1) / ssmk::kWave;
@@ -450,15 +471,18 @@ BwdPlan make_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t super
     return o;
   };
   const size_t bt = size_t(Bt), d = size_t(D), n = size_t(N);
-  pl.off_hcar = take(bt * size_t(pl.Cf - 1) * d * n * 4);
-  pl.off_dsumf = take(bt * size_t(pl.Cf - 1) * d * 4);
+  // the forward states every 16 steps and their pass's buffers (none when
+  // the caller hands in the forward scan's kept states)
+  const size_t nf = saved ? 0 : size_t(pl.Cf - 1);
+  pl.off_hcar = take(bt * nf * d * n * 4);
+  pl.off_dsumf = take(bt * nf * d * 4);
   pl.off_gsum = take(bt * size_t(pl.Cs - 1) * d * n * 4);
   pl.off_dsums = take(bt * size_t(pl.Cs - 1) * d * 4);
   pl.off_dAp = take(bt * size_t(pl.Cs) * d * n * 4);
   pl.off_dDp = take(bt * size_t(pl.Cs) * d * 4);
   pl.off_dBp = take(bt * size_t(L) * size_t(pl.dtiles) * n * 4);
   pl.off_dCp = take(bt * size_t(L) * size_t(pl.dtiles) * n * 4);
-  pl.grp = grouping(pl.Cf - 1, Bt * D * N);
+  if (!saved) pl.grp = grouping(pl.Cf - 1, Bt * D * N);
   pl.off_gS = take(bt * size_t(pl.grp.G) * d * 4);
   pl.off_gB = take(bt * size_t(pl.grp.G) * d * n * 4);
   pl.total = off;
@@ -488,7 +512,8 @@ ssm_status_t check_bwd(const ssm_scan_bwd_args_t* a, BwdPlan* plan) {
       !mul_ok(a->batch, dn, &bdn) || !mul_ok(bln, dtiles, &blt) || bld > INT64_MAX / 8 ||
       blt > INT64_MAX / 8 || bdn > INT64_MAX / 8)
     return fail(SSM_ERR_SHAPE, "sizes overflow");
-  *plan = make_bwd_plan(a->batch, a->seqlen, a->dim, a->dstate, a->super_chunk);
+  *plan = make_bwd_plan(a->batch, a->seqlen, a->dim, a->dstate, a->super_chunk,
+                        a->h_saved != nullptr);
   if (!a->A || !a->dA) return fail(SSM_ERR_NULL, "A and dA are required");
   const bool work = a->seqlen > 0 && a->batch * a->dim > 0;
   if (work && (!a->x || !a->delta || !a->Bm || !a->Cm || !a->dy || !a->dx || !a->ddelta ||
@@ -500,13 +525,14 @@ ssm_status_t check_bwd(const ssm_scan_bwd_args_t* a, BwdPlan* plan) {
       misaligned(a->Dskip, 4) || misaligned(a->h0, 4) || misaligned(a->dh_last, 4) ||
       misaligned(a->dx, 4) || misaligned(a->ddelta, 4) || misaligned(a->dA, 4) ||
       misaligned(a->dB, 4) || misaligned(a->dC, 4) || misaligned(a->dD, 4) ||
-      misaligned(a->dh0, 4) || misaligned(a->workspace, 256))
+      misaligned(a->dh0, 4) || misaligned(a->workspace, 256) || misaligned(a->h_saved, 4))
     return fail(SSM_ERR_UNSUPPORTED,
                 "misaligned pointer (element alignment; B, C 4 bytes; workspace 256 bytes)");
   const Range ins[] = {
       {a->x, size_t(bld) * in_sz},   {a->delta, size_t(bld) * in_sz}, {a->A, size_t(dn) * 4},
       {a->Bm, size_t(bln) * in_sz},  {a->Cm, size_t(bln) * in_sz},    {a->Dskip, size_t(a->dim) * 4},
       {a->h0, size_t(bdn) * 4},      {a->dy, size_t(bld) * in_sz},    {a->dh_last, size_t(bdn) * 4},
+      {a->h_saved, size_t(bdn) * size_t(saved_count(a->seqlen)) * 4},
   };
   const Range outs[] = {
       {a->dx, size_t(bld) * 4}, {a->ddelta, size_t(bld) * 4}, {a->dA, size_t(dn) * 4},
@@ -542,9 +568,10 @@ ssm_status_t run_bwd(const ssm_scan_bwd_args_t* a, const BwdPlan& pl, hipStream_
   using namespace ssmk;
   char* ws = static_cast<char*>(a->workspace);
   const float thr = exact_threshold(a->disc, a->in_dtype);
-  // forward states entering every 16-step chunk: the forward summary and
-  // carry passes run at that chunk length
-  if (pl.Cf > 1) {
+  // forward states entering every 16-step chunk: kept by the forward scan,
+  // or from the forward summary and carry passes run at that chunk length
+  const bool saved = a->h_saved != nullptr;
+  if (pl.Cf > 1 && !saved) {
     ScanParams fp{};
     fp.x = a->x;
     fp.delta = a->delta;
@@ -586,7 +613,7 @@ ssm_status_t run_bwd(const ssm_scan_bwd_args_t* a, const BwdPlan& pl, hipStream_
   bp.dC = a->dC;
   bp.dD = a->dD;
   bp.dh0 = a->dh0;
-  bp.hcar = reinterpret_cast<const float*>(ws + pl.off_hcar);
+  bp.hcar = saved ? a->h_saved : reinterpret_cast<const float*>(ws + pl.off_hcar);
   bp.gsum = reinterpret_cast<float*>(ws + pl.off_gsum);
   bp.dsum_s = reinterpret_cast<float*>(ws + pl.off_dsums);
   bp.dAp = reinterpret_cast<float*>(ws + pl.off_dAp);
@@ -715,6 +742,8 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_args_t* a, void* hip_stream) {
   kp.z = a->z;
   kp.cs_in = a->conv_w ? a->conv_state_in : nullptr;
   kp.cs_out = a->conv_w ? a->conv_state_out : nullptr;
+  kp.nsave = saved_count(a->seqlen);
+  kp.hsave = kp.nsave > 0 ? a->h_saved : nullptr;
   switch (a->dstate) {
     case 1: return dispatch_types<1>(a, kp, pl, s);
     case 2: return dispatch_types<2>(a, kp, pl, s);
@@ -765,7 +794,9 @@ size_t ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args_t* a) {
   if (!mul_ok(a->batch, a->seqlen, &bl) || !mul_ok(bl, a->dim, &bld) ||
       !mul_ok(bl, a->dstate, &bln) || bln > INT64_MAX / 64)
     return 0;
-  return make_bwd_plan(a->batch, a->seqlen, a->dim, a->dstate, a->super_chunk).total;
+  return make_bwd_plan(a->batch, a->seqlen, a->dim, a->dstate, a->super_chunk,
+                       a->h_saved != nullptr)
+      .total;
 }
 
 ssm_status_t ssm_scan_bwd(const ssm_scan_bwd_args_t* a, void* hip_stream) {

@@ -84,7 +84,7 @@ def test_struct_layout_matches_header(tmp_path):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_abi_version() == 2
+    assert lib.ssm_abi_version() == 3
     for s in range(0, 8):
         assert lib.ssm_status_string(s)
     assert lib.ssm_status_string(99) == b"unknown status"
@@ -339,6 +339,68 @@ def test_step_fused_errors(lib):
     s = valid_step_args()
     s.z = s.y
     assert step_call(lib, s) == ssm.SSM_ERR_ALIAS
+
+
+# ---------------------------------------------------------------------------
+# states kept for the backward pass (h_saved)
+# ---------------------------------------------------------------------------
+
+SAVED = 0x100000000 + 30 * GB
+
+
+def test_binding_abi_matches_header():
+    m = re.search(r"#define SSM_ABI_VERSION (\d+)", open(HEADER).read())
+    assert int(m.group(1)) == ssm.ABI_VERSION
+
+
+def test_saved_states_shape():
+    assert ssm.saved_states_shape(2, 0, 8, 16) == (2, 0, 8, 16)
+    assert ssm.saved_states_shape(2, 16, 8, 16) == (2, 0, 8, 16)
+    assert ssm.saved_states_shape(2, 17, 8, 16) == (2, 1, 8, 16)
+    assert ssm.saved_states_shape(2, 64, 8, 16) == (2, 3, 8, 16)
+    assert ssm.saved_states_shape(1, 65, 8, 4) == (1, 4, 8, 4)
+
+
+@pytest.mark.parametrize("cl", [7, 9, 30])
+def test_saved_states_need_chunks_of_four(lib, cl):
+    a = valid_scan_args(batch=1, L=256, D=64, chunk_len=cl)
+    a.h_saved = SAVED
+    expect(lib, a, ssm.SSM_ERR_UNSUPPORTED)
+
+
+@pytest.mark.parametrize("L,cl", [(256, 0), (256, 8), (256, 100), (255, 1000), (255, 255)])
+def test_saved_states_chunk_ok(lib, L, cl):
+    # a split scan with chunks of a multiple of 4, or an unsplit one of any
+    # length, passes the chunk check and stops at the alias check
+    a = valid_scan_args(batch=1, L=L, D=64, chunk_len=cl)
+    a.h_saved = a.y + 4
+    expect(lib, a, ssm.SSM_ERR_ALIAS)
+
+
+@pytest.mark.parametrize("other", ["x", "Bm", "h0", "y", "h_last", "workspace"])
+def test_saved_states_alias(lib, other):
+    a = valid_scan_args(batch=1, L=4096, D=64)
+    a.h_saved = getattr(a, other) + 4
+    expect(lib, a, ssm.SSM_ERR_ALIAS)
+
+
+def test_saved_states_misaligned(lib):
+    a = valid_scan_args()
+    a.h_saved = SAVED + 2
+    expect(lib, a, ssm.SSM_ERR_UNSUPPORTED)
+
+
+def test_bwd_saved_states(lib):
+    a = valid_bwd_args(batch=8, L=2048, D=1536, N=16)
+    full = lib.ssm_scan_bwd_workspace_size(ctypes.byref(a))
+    a.h_saved = SAVED
+    saved = lib.ssm_scan_bwd_workspace_size(ctypes.byref(a))
+    # the 16-step forward carries (and their Delta sums) are not needed
+    assert full - saved >= 8 * 127 * 1536 * (16 + 1) * 4
+    a.h_saved = a.dx + 4                   # an input over a gradient
+    assert bwd_call(lib, a) == ssm.SSM_ERR_ALIAS
+    a.h_saved = SAVED + 2
+    assert bwd_call(lib, a) == ssm.SSM_ERR_UNSUPPORTED
 
 
 # ---------------------------------------------------------------------------
