@@ -519,6 +519,20 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
 
   static_assert(kU % 2 == 0, "row buffers alternate within a block");
   const int32_t nblk = steps / kU;
+  // SAVE: the state entering step te = t0 + (blk + 1) kU is kept when te is
+  // a multiple of kSaveStride below L (chunks start on multiples of kU, so
+  // these steps end blocks; the remainder after the last block holds none).
+  // The lane's destination row advances in registers; the blocks that save
+  // are every kSaveStride / kU-th from save_blk on, below save_lim.
+  int32_t save_blk = 0, save_lim = 0;
+  float* save_dst = nullptr;
+  if constexpr (SAVE) {
+    const int64_t first = (t0 / kSaveStride + 1) * kSaveStride;   // first kept step > t0
+    save_blk = static_cast<int32_t>((first - t0) / kU) - 1;
+    const int64_t lim = (p.L - 1 - t0) / kU;                      // te < L  <=>  blk < lim
+    save_lim = static_cast<int32_t>(lim < nblk ? lim : nblk);
+    save_dst = p.hsave + ((b * p.nsave + first / kSaveStride - 1) * D + d) * N;
+  }
   float xc[kU], dc[kU], zc[kU];
   constexpr InT* kIn = nullptr;
   // byte offset of row t of the chunk, clamped to its last row: rows past the
@@ -557,14 +571,11 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
       one_step(xc[j + 1], dc[j + 1], zc[j + 1], tb + j + 2 < steps, Bb1, Bb0, Cb1, Cb0);
     }
     if constexpr (SAVE) {
-      // keep the state entering step te when te is a multiple of kSaveStride
-      // (chunks start on multiples of kU, so such steps end a block; the
-      // remainder after the last block holds none below L)
-      const int64_t te = t0 + tb + kU;
-      if (te % kSaveStride == 0 && te < p.L) {
-        float* dst = p.hsave + ((b * p.nsave + te / kSaveStride - 1) * D + d) * N;
+      if (blk == save_blk && blk < save_lim) {
 #pragma unroll
-        for (int n = 0; n < N; ++n) dst[n] = h[n];
+        for (int n = 0; n < N; ++n) save_dst[n] = h[n];
+        save_dst += D * N;
+        save_blk += kSaveStride / kU;
       }
     }
     if constexpr (!OUT) {
