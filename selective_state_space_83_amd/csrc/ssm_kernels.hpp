@@ -837,7 +837,8 @@ struct StepLayout {
   static constexpr int NL = N < 4 ? N : 4;
   static constexpr int S = N / NL;
   static constexpr int CPW = kWave / S;   // channels per wave
-  static constexpr int ROWS = 2;          // batch rows per wave (more state in flight)
+  static constexpr int ROWS = 2;   // batch rows per wave, loaded before any is computed
+  static constexpr int WPG = 4;    // waves per workgroup (consecutive channel tiles)
 };
 
 __device__ __forceinline__ float dpp_quad_xor1(float v) {
@@ -881,13 +882,19 @@ __device__ __forceinline__ void store_state(float* p, const float (&h)[NL]) {
 // identical values.  The optional conv window, step-size transform and gate
 // are wave-uniform branches (this kernel is bound by the state traffic).
 template <int N, typename InT, typename OutT, int DISC>
-__global__ void __launch_bounds__(kWave) k_step(const StepParams p) {
+__global__ void __launch_bounds__(kWave * StepLayout<N>::WPG) k_step(const StepParams p) {
   constexpr int NL = StepLayout<N>::NL, S = StepLayout<N>::S, CPW = StepLayout<N>::CPW;
-  constexpr int ROWS = StepLayout<N>::ROWS;
+  constexpr int ROWS = StepLayout<N>::ROWS, WPG = StepLayout<N>::WPG;
   const int wg = xcd_remap(blockIdx.x, p.nwg);
-  const int64_t bt = wg / p.dtiles;
-  const int64_t dtile = wg - bt * p.dtiles;
-  const int lane = threadIdx.x;
+  const int64_t gtiles = (p.dtiles + WPG - 1) / WPG;
+  const int64_t bt = wg / gtiles;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const int64_t dtile = (wg - bt * gtiles) * WPG + w;
+  // a wave past the last tile exits: a wave duplicating another wave's
+  // channels would race with its in-place state update (this kernel has no
+  // barrier, so an early exit is safe)
+  if (dtile >= p.dtiles) return;
+  const int lane = threadIdx.x % kWave;
   const int j = lane % S;
   int64_t d = dtile * CPW + lane / S;
   if (d > p.D - 1) d = p.D - 1;
@@ -906,51 +913,65 @@ __global__ void __launch_bounds__(kWave) k_step(const StepParams p) {
     for (int k = 0; k < K; ++k) cw[kConvTaps - K + k] = p.conv_w[d * K + k];
     cb = p.conv_b ? p.conv_b[d] : 0.0f;
   }
+  // Every row's loads are issued before any row is computed or stored (the
+  // stores could otherwise alias the next row's loads as far as the compiler
+  // knows, and would hold them back): ROWS x 1 KB of state per wave in
+  // flight.  Rows past the batch read row Bt - 1 and store nothing.
+  float h[ROWS][NL], Bv[ROWS][NL], Cv[ROWS][NL], u[ROWS], dv[ROWS], zg[ROWS];
+  float xw[ROWS][3];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    int64_t b = bt * ROWS + r;
+    if (b > p.Bt - 1) b = p.Bt - 1;
+    load_state<NL>(h[r], p.h + (b * p.D + d) * N + n0);
+    const InT* Bp = static_cast<const InT*>(p.Bm) + b * N + n0;
+    const InT* Cp = static_cast<const InT*>(p.Cm) + b * N + n0;
+#pragma unroll
+    for (int n = 0; n < NL; ++n) {
+      Bv[r][n] = ld(Bp + n);
+      Cv[r][n] = ld(Cp + n);
+    }
+    u[r] = ld(static_cast<const InT*>(p.x) + b * p.D + d);
+    dv[r] = ld(static_cast<const InT*>(p.delta) + b * p.D + d);
+    zg[r] = p.z ? ld(static_cast<const InT*>(p.z) + b * p.D + d) : 0.0f;
+    if (K > 0) {
+      // window x[-SW .. -1] (oldest first) as x[-3], x[-2], x[-1] (zero
+      // where the window is shorter); three independent loads
+      const float* win = p.conv_state + (b * p.D + d) * SW;
+      xw[r][0] = SW >= 3 ? win[SW - 3] : 0.0f;
+      xw[r][1] = SW >= 2 ? win[SW - 2] : 0.0f;
+      xw[r][2] = SW >= 1 ? win[SW - 1] : 0.0f;
+    }
+  }
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     const int64_t b = bt * ROWS + r;
     if (b >= p.Bt) break;
-    float* hp = p.h + (b * p.D + d) * N + n0;
-    float h[NL];
-    load_state<NL>(h, hp);
-    const InT* Bp = static_cast<const InT*>(p.Bm) + b * N + n0;
-    const InT* Cp = static_cast<const InT*>(p.Cm) + b * N + n0;
-    float Bv[NL], Cv[NL];
-#pragma unroll
-    for (int n = 0; n < NL; ++n) {
-      Bv[n] = ld(Bp + n);
-      Cv[n] = ld(Cp + n);
-    }
-    float u = ld(static_cast<const InT*>(p.x) + b * p.D + d);
-    float dv = ld(static_cast<const InT*>(p.delta) + b * p.D + d);
-    if (dtm != kDtRaw) dv = dt_transform(dv, dtb, dtm);
+    float ur = u[r];
+    float dvr = dv[r];
+    if (dtm != kDtRaw) dvr = dt_transform(dvr, dtb, dtm);
     if (K > 0) {
-      // window x[-SW .. -1] (oldest first) as x[-3], x[-2], x[-1] (zero where
-      // the window is shorter), then the new input; three independent loads
-      float* win = p.conv_state + (b * p.D + d) * SW;
-      const float xm3 = SW >= 3 ? win[SW - 3] : 0.0f;
-      const float xm2 = SW >= 2 ? win[SW - 2] : 0.0f;
-      const float xm1 = SW >= 1 ? win[SW - 1] : 0.0f;
-      float zc = fmaf(cw[3], u, cb);
-      zc = fmaf(cw[2], xm1, zc);
-      zc = fmaf(cw[1], xm2, zc);
-      zc = fmaf(cw[0], xm3, zc);
-      // the window moves on by one input (written by one lane per channel,
-      // after every lane of the wave has read it in the loads above)
+      float zc = fmaf(cw[3], ur, cb);
+      zc = fmaf(cw[2], xw[r][2], zc);
+      zc = fmaf(cw[1], xw[r][1], zc);
+      zc = fmaf(cw[0], xw[r][0], zc);
+      // the window moves on by one input (written by one lane per channel;
+      // every lane of the wave read it above)
       if (j == 0) {
-        if (SW >= 3) win[SW - 3] = xm2;
-        if (SW >= 2) win[SW - 2] = xm1;
-        if (SW >= 1) win[SW - 1] = u;
+        float* win = p.conv_state + (b * p.D + d) * SW;
+        if (SW >= 3) win[SW - 3] = xw[r][1];
+        if (SW >= 2) win[SW - 2] = xw[r][2];
+        if (SW >= 1) win[SW - 1] = ur;
       }
-      u = silu(zc);
+      ur = silu(zc);
     }
-    float acc = ssm_step_any<NL, DISC, true>(h, cc, Bv, Cv, u, dv);
+    float acc = ssm_step_any<NL, DISC, true>(h[r], cc, Bv[r], Cv[r], ur, dvr);
     if constexpr (S >= 2) acc += dpp_quad_xor1(acc);
     if constexpr (S >= 4) acc += dpp_quad_xor2(acc);
-    store_state<NL>(hp, h);
+    store_state<NL>(p.h + (b * p.D + d) * N + n0, h[r]);
     if (j == 0) {
-      float yv = fmaf(dsk, u, acc);
-      if (p.z) yv *= silu(ld(static_cast<const InT*>(p.z) + b * p.D + d));
+      float yv = fmaf(dsk, ur, acc);
+      if (p.z) yv *= silu(zg[r]);
       st(static_cast<OutT*>(p.y) + b * p.D + d, yv);
     }
   }

@@ -402,15 +402,15 @@ ssm_status_t dispatch_types(const ssm_scan_args_t* a, const ssmk::ScanParams& kp
 template <int N, typename InT, typename OutT>
 ssm_status_t run_step_t(const ssm_step_args_t* a, ssmk::StepParams kp, hipStream_t s) {
   constexpr int cpw = ssmk::StepLayout<N>::CPW;
-  constexpr int rows = ssmk::StepLayout<N>::ROWS;
+  constexpr int rows = ssmk::StepLayout<N>::ROWS, wpg = ssmk::StepLayout<N>::WPG;
   kp.dtiles = int32_t((a->dim + cpw - 1) / cpw);
-  kp.nwg = int32_t((a->batch + rows - 1) / rows * kp.dtiles);
+  kp.nwg = int32_t((a->batch + rows - 1) / rows * ((kp.dtiles + wpg - 1) / wpg));
   if (a->disc == SSM_DISC_ZOH)
-    hipLaunchKernelGGL((ssmk::k_step<N, InT, OutT, ssmk::kZoh>), dim3(kp.nwg), dim3(ssmk::kWave), 0,
-                       s, kp);
+    hipLaunchKernelGGL((ssmk::k_step<N, InT, OutT, ssmk::kZoh>), dim3(kp.nwg),
+                       dim3(ssmk::kWave * wpg), 0, s, kp);
   else
-    hipLaunchKernelGGL((ssmk::k_step<N, InT, OutT, ssmk::kDeltaB>), dim3(kp.nwg), dim3(ssmk::kWave),
-                       0, s, kp);
+    hipLaunchKernelGGL((ssmk::k_step<N, InT, OutT, ssmk::kDeltaB>), dim3(kp.nwg),
+                       dim3(ssmk::kWave * wpg), 0, s, kp);
   return launch_status("k_step");
 }
 
