@@ -124,3 +124,60 @@ def test_bwd_empty_sequence():
     torch.cuda.synchronize()
     assert torch.count_nonzero(g["dA"]).item() == 0 and torch.count_nonzero(g["dD"]).item() == 0
     assert torch.equal(g["dh0"], dhl)
+
+
+def test_bwd_workload_fp32_full():
+    """The bench's backward at full size (batch 8, L 2048, D 1536, N 16,
+    fp32): the same seeded inputs and upstream gradients, the forward keeping
+    its states and the backward started from them, every gradient compared
+    with the oracle element by element."""
+    w = SI.WORKLOADS["fp32"]
+    G.say("workload", w)
+    inp = SI.scan_inputs(w, h0=True)
+    gi = SI.grad_inputs(w)
+    t = {k: G.dev(inp[k]) for k in ("x", "delta", "B", "C")}
+    A, Dv, h0 = G.dev(inp["A"]), G.dev(inp["D"]), G.dev(inp["h0"])
+    dy, dhl = G.dev(gi["dy"]), G.dev(gi["dh_last"])
+    hs = torch.empty(ssm.saved_states_shape(w.batch, w.seqlen, w.dim, w.dstate), device="cuda")
+    fwd, _, _ = ssm.prepare_scan(t["x"], t["delta"], A, t["B"], t["C"], Dv, h0=h0, h_saved=hs)
+    bwd, g = ssm.prepare_bwd(t["x"], t["delta"], A, t["B"], t["C"], dy, D=Dv, h0=h0,
+                             dh_last=dhl, h_saved=hs)
+    fwd.run()
+    bwd.run()
+    torch.cuda.synchronize()
+    ref = oracle.default().scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                                    gi["dy"], D=inp["D"], h0=inp["h0"], dh_last=gi["dh_last"],
+                                    nthreads=G.threads())
+    for k in GRADS:
+        G.say(compare_grad(g[k].cpu().numpy(), ref[k], "f32", k))
+
+
+def test_bwd_workload_long_sampled():
+    """The long workload's backward (batch 1, L 2^20, D 512, N 16, bf16) from
+    kept states, on sampled channels: dx, dDelta, dA[d], dD[d] and dh0[d] of
+    a channel depend on that channel's inputs (and the shared B, C) only, so
+    the oracle runs on the channel slices.  (dB and dC sum over all channels;
+    the full-size fp32 test covers them.)"""
+    w = SI.WORKLOADS["long"]
+    G.say("workload", w)
+    inp = SI.scan_inputs(w, h0=True)
+    gi = SI.grad_inputs(w)
+    t = {k: G.dev(inp[k], "bf16") for k in ("x", "delta", "B", "C")}
+    A, Dv, h0 = G.dev(inp["A"]), G.dev(inp["D"]), G.dev(inp["h0"])
+    dy, dhl = G.dev(gi["dy"], "bf16"), G.dev(gi["dh_last"])
+    hs = torch.empty(ssm.saved_states_shape(w.batch, w.seqlen, w.dim, w.dstate), device="cuda")
+    ssm.scan(t["x"], t["delta"], A, t["B"], t["C"], Dv, h0=h0, h_saved=hs)
+    g = ssm.scan_bwd(t["x"], t["delta"], A, t["B"], t["C"], dy, D=Dv, h0=h0, dh_last=dhl,
+                     h_saved=hs)
+    torch.cuda.synchronize()
+    ds = [0, 131, 257, 511]
+    sub = G.channel_slice(inp, 0, ds)
+    ref = oracle.default().scan_bwd(sub["x"], sub["delta"], sub["A"], sub["B"], sub["C"],
+                                    np.ascontiguousarray(gi["dy"][:, :, ds]), D=sub["D"],
+                                    h0=sub["h0"],
+                                    dh_last=np.ascontiguousarray(gi["dh_last"][:, ds]),
+                                    nthreads=G.threads())
+    got = {"dx": g["dx"][:, :, ds], "ddelta": g["ddelta"][:, :, ds], "dA": g["dA"][ds],
+           "dD": g["dD"][ds], "dh0": g["dh0"][:, ds]}
+    for k, v in got.items():
+        G.say(compare_grad(v.cpu().numpy(), ref[k], "bf16", k))
