@@ -17,18 +17,19 @@
 // carry walk, and a main pass that starts each super-chunk from its carry.
 //
 // The main pass needs h_{t-1} at every step, in reverse order.  It takes the
-// forward state at every 16th step from the forward summary and carry passes
-// (run at a 16-step chunk), recomputes each 16-step chunk forwards into
-// registers and then walks it backwards, so the (batch, L, D, N) states are
-// never written to memory (the memory argument of the pages' hardware-aware
-// scan: explainer section 3.4).
+// forward state at every 16th step (kept by the forward scan, or from the
+// forward summary and carry passes run at a 16-step chunk), recomputes each
+// 16-step chunk forwards into registers and then walks it backwards, so the
+// (batch, L, D, N) states are never written to memory (the memory argument
+// of the pages' hardware-aware scan: explainer section 3.4).
 //
 // Layout of the main pass: lane = channel, wave = 4 states (NS) of 64
 // channels, workgroup = the N / NS waves of one (batch row, 64-channel tile,
-// super-chunk).  Every 4 steps two reductions go through LDS: over the 64
-// channels of a wave (dB, dC; written as per-tile partials) and over the
-// waves of the workgroup (du, dDelta).  Partials are summed in a fixed
-// order by small reduction kernels, so results are deterministic.
+// super-chunk).  Two reductions go through LDS: every 2 steps, over the 64
+// channels of a wave (dB, dC; wave-private rows, written as per-tile
+// partials), and every 4 steps over the waves of the workgroup (du, dDelta;
+// one barrier per 4 steps).  Partials are summed in a fixed order by small
+// reduction kernels, so results are deterministic.
 #pragma once
 
 #include "ssm_kernels.hpp"
