@@ -152,3 +152,50 @@ def test_backward_from_kept_states(case):
         got = g_saved[k].cpu().numpy()
         compare_grad(got, ref[k], idt, k)
         compare_grad(got, g_own[k].cpu().numpy(), idt, k + " (vs recomputed states)")
+
+
+def _in_canary(shape, pad, canary, dtype=torch.float32):
+    n = int(np.prod(shape))
+    buf = torch.full((n + 2 * pad,), canary, dtype=dtype, device="cuda")
+    return buf, buf[pad:pad + n].view(*shape)
+
+
+def test_no_writes_outside_kept_states_and_gradients():
+    """h_saved, every gradient and the backward workspace sit inside larger
+    buffers filled with a canary; after the forward (keeping states, split
+    into chunks) and the backward from the kept states, every canary is
+    unchanged and the gradients still match the oracle."""
+    import ctypes
+    Bt, L, D, N = 2, 333, 70, 16
+    w = SI.Workload("canary", 150, Bt, L, D, N, "f32", "f32", a_dist="random")
+    inp = SI.scan_inputs(w, h0=True)
+    gi = SI.grad_inputs(w)
+    t = {k: G.dev(inp[k]) for k in ("x", "delta", "B", "C", "A", "D", "h0")}
+    dy, dhl = G.dev(gi["dy"]), G.dev(gi["dh_last"])
+    pad, canary = 4096, -12345.5
+    hs_buf, hs = _in_canary(ssm.saved_states_shape(Bt, L, D, N), pad, canary)
+    ssm.scan(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], h0=t["h0"], chunk_len=40,
+             h_saved=hs)
+    shapes = {"dx": (Bt, L, D), "ddelta": (Bt, L, D), "dA": (D, N), "dB": (Bt, L, N),
+              "dC": (Bt, L, N), "dD": (D,), "dh0": (Bt, D, N)}
+    bufs, grads = {}, {}
+    for k, shp in shapes.items():
+        bufs[k], grads[k] = _in_canary(shp, pad, canary)
+    args = ssm.make_bwd_args(t["x"], t["delta"], t["A"], t["B"], t["C"], dy, t["D"], t["h0"],
+                             dhl, False, grads, 0, hs)
+    lib = ssm.load_library()
+    need = int(lib.ssm_scan_bwd_workspace_size(ctypes.byref(args)))
+    wbuf = torch.full((need + 2 * pad,), 0xA5, dtype=torch.uint8, device="cuda")
+    args.workspace = wbuf[pad:pad + need].data_ptr()
+    args.workspace_bytes = need
+    status = lib.ssm_scan_bwd(ctypes.byref(args), torch.cuda.current_stream().cuda_stream)
+    assert status == 0, lib.ssm_last_error_message()
+    torch.cuda.synchronize()
+    for name, buf in [("h_saved", hs_buf)] + list(bufs.items()):
+        assert torch.all(buf[:pad] == canary) and torch.all(buf[-pad:] == canary), name
+    assert torch.all(wbuf[:pad] == 0xA5) and torch.all(wbuf[-pad:] == 0xA5), "workspace"
+    ref = oracle.default().scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                                    gi["dy"], D=inp["D"], h0=inp["h0"], dh_last=gi["dh_last"],
+                                    nthreads=G.threads())
+    for k in shapes:
+        compare_grad(grads[k].cpu().numpy(), ref[k], "f32", k)
