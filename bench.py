@@ -58,6 +58,7 @@ HBM_PEAK_GBS = 8000.0
 FUSED_DECODE_CONV_K = 4                    # conv taps of the fused decode run
 SLOT_PEAK = 256 * 4 * 16 * 2.4e9          # VALU lane-slots per second
 KERNEL_SRC = os.path.join(ROOT, "selective_state_space_83_amd", "csrc", "ssm_kernels.hpp")
+BWD_SRC = os.path.join(ROOT, "selective_state_space_83_amd", "csrc", "ssm_bwd.hpp")
 
 
 def log(*a):
@@ -140,7 +141,7 @@ def algorithmic_slots(w, fused=False) -> float:
 
 def traffic_record(workload: str, kernel: str = "k_scan_out"):
     """HBM traffic per launch of `kernel` from committed rocprofv3 --pmc
-    summaries, valid only if the kernel source is unchanged since they were
+    summaries, valid only if the kernel sources are unchanged since they were
     taken."""
     path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
     if not os.path.exists(path):
@@ -149,6 +150,10 @@ def traffic_record(workload: str, kernel: str = "k_scan_out"):
     src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
     if rec.get("kernel_source_sha256") != src_hash:
         return None
+    if "bwd_source_sha256" in rec:
+        bwd_hash = hashlib.sha256(open(BWD_SRC, "rb").read()).hexdigest()
+        if rec["bwd_source_sha256"] != bwd_hash:
+            return None
     return rec.get("bytes_per_launch")
 
 
@@ -470,7 +475,9 @@ def main():
         slots = w.elems * SLOTS_BWD_ELEM[w.zoh]
         alu = slots / (main_us * 1e-6) / 1e12
         roof = {"bound": "alu", "achieved": alu, "peak": SLOT_PEAK / 1e12,
-                "unit": "T lane-slot/s", "frac": alu / (SLOT_PEAK / 1e12), "traffic": None,
+                "unit": "T lane-slot/s", "frac": alu / (SLOT_PEAK / 1e12),
+                "traffic": traffic_record(w.name, "k_bwd_main") if kept and not args.train
+                else None,
                 "kernel": "k_bwd_main", "kernel_us": main_us}
         out = {"metric": METRIC, "value": w.elems / (ms * 1e-3), "unit": "elem/s", "n_gpus": 1,
                "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
