@@ -88,6 +88,9 @@ SAVED_FWD = [
     (1, 16, 32, 2, "f32", False, 0, ()),           # nothing to keep
     (2, 130, 64, 16, "f32", True, 0, ("softplus", "gate", "state")),
     (1, 300, 96, 16, "bf16", False, 64, ("bias", "gate")),
+    (2, 101, 33, 16, "f32", False, 4, ()),         # chunks of one block
+    (1, 50, 70, 2, "bf16", True, 8, ()),
+    (2, 67, 40, 8, "f32", True, 12, ("state",)),   # conv window, chunks of 3 blocks
 ]
 
 
@@ -122,6 +125,9 @@ SAVED_BWD = [
     (4, 1000, 128, 16, "f32", False, 0),
     (1, 4097, 64, 4, "bf16", True, 256),
     (2, 2048, 256, 16, "bf16", True, 0),
+    (2, 16, 40, 16, "f32", False, 0),               # nothing kept
+    (3, 17, 65, 2, "bf16", True, 0),
+    (2, 333, 96, 8, "f32", True, 48),
 ]
 
 
