@@ -1,6 +1,7 @@
 // ssm_kernels.hpp -- gfx950 device code of the selective state-space scan.
 //
-// Work decomposition (all kernels use one 64-lane wave per workgroup):
+// Work decomposition of the scan (its kernels use one 64-lane wave per
+// workgroup; the decode step and the backward pass have their own layouts):
 //   * lane  = one channel (b, d); the lane keeps all N states of that channel
 //     in VGPRs for the whole chunk, so the expanded (batch, L, D, N) state is
 //     never written anywhere (the memory argument of the pages'
@@ -18,9 +19,12 @@
 //       k_carry_combine  per (b, d, n), the carries into every chunk by the
 //                        associative operator (a, b) o (a', b') = (a a', a' b + b')
 //                        (53ai.com explainer section 3.3: split the sequence,
-//                        scan the parts, combine and adjust);
+//                        scan the parts, combine and adjust); long chains of
+//                        few (b, d, n) are walked in groups instead;
 //       k_scan_out       per chunk, the recurrence again from its carry-in,
-//                        writing y (and h_last from the final chunk).
+//                        writing y (and h_last from the final chunk, and
+//                        optionally the state every 16 steps for the
+//                        backward pass).
 //     The chunk's decay factor is exp(A * sum Delta), the product of its
 //     per-step Abar factors.
 //
@@ -369,10 +373,7 @@ __device__ __forceinline__ Tile tile_of(int wg, int64_t dtiles, int64_t nchunks)
 // further ahead to cover the same memory latency.
 constexpr int kUnrollOut = 4;
 static_assert(kSaveStride % kUnrollOut == 0, "kept states fall on block ends");
-#ifndef SSM_UNROLL_SUM
-#define SSM_UNROLL_SUM 8
-#endif
-constexpr int kUnrollSum = SSM_UNROLL_SUM;
+constexpr int kUnrollSum = 8;   // (4 and 6 measured the same on the fp32, conv and long scans)
 
 // Streams through buffer resources: the wave-uniform chunk base and size sit
 // in an SGPR descriptor, the lane's byte offset is a constant VGPR and the
