@@ -9,8 +9,10 @@ called through the C ABI via the binding:
 Small shapes span several 64-channel tiles, ragged tails and forced chunk
 plans (including chunks shorter than the conv window); a sequence split
 across calls and a prefill handed to decode steps are compared with one
-oracle scan of the whole sequence; the conv workload runs at full size with
-every fused step on.
+oracle scan of the whole sequence.  Each workload the bench runs with fused
+steps is checked at full size in the bench's launch configuration: conv and
+fp32 element by element, long on sampled channels, decode (512 tokens) on
+sampled channels token by token.
 """
 from __future__ import annotations
 
@@ -231,3 +233,83 @@ def test_workload_conv_fused_full():
     G.say(G.compare(y, y_ref, G.TOL["bf16"], "conv fused y"),
           G.compare(hl, h_ref, G.TOL["bf16"], "conv fused h_last"))
     assert np.array_equal(cs, cs_ref.astype(np.float32))
+
+
+BENCH_SCAN_FUSED = frozenset({"softplus", "gate"})   # the fused bench run without a conv
+
+
+def test_workload_fp32_fused_full():
+    """The fp32 workload (8 x 2048 x 1536 x 16) at full size with the fused
+    steps of its bench run (softplus step size with bias, output gate), in
+    the launch configuration of the library's plan, compared element by
+    element."""
+    w = SI.WORKLOADS["fp32"]
+    inp = SI.scan_inputs(w)
+    ex = SI.fused_inputs(w)
+    G.say("workload fp32, fused", w)
+    y, hl, _ = G.gpu_scan_fused(inp, ex, BENCH_SCAN_FUSED, "f32", "f32", zoh=False, h0=False)
+    y_ref, h_ref, _ = G.oracle_scan_fused(inp, ex, BENCH_SCAN_FUSED, zoh=False, h0=False)
+    G.say(G.compare(y, y_ref, G.TOL["f32"], "fp32 fused y"),
+          G.compare(hl, h_ref, G.TOL["f32"], "fp32 fused h_last"))
+
+
+def test_workload_long_fused_sampled():
+    """The long workload (1 x 2^20 x 512 x 16, bf16) at full size with the
+    fused steps of its bench run; the oracle runs on sampled channels, whose
+    outputs depend on their own inputs and the shared B, C only."""
+    w = SI.WORKLOADS["long"]
+    inp = SI.scan_inputs(w)
+    ex = SI.fused_inputs(w)
+    G.say("workload long, fused", w)
+    y, hl, _ = G.gpu_scan_fused(inp, ex, BENCH_SCAN_FUSED, w.in_dtype, w.out_dtype, zoh=w.zoh,
+                                h0=False)
+    ds = [0, 1, 63, 64, 300, 511]
+    sub = G.channel_slice(inp, 0, ds)
+    sub_ex = {"delta_raw": np.ascontiguousarray(ex["delta_raw"][0:1, :, ds]),
+              "z": np.ascontiguousarray(ex["z"][0:1, :, ds]),
+              "delta_bias": np.ascontiguousarray(ex["delta_bias"][ds])}
+    y_ref, h_ref, _ = G.oracle_scan_fused(sub, sub_ex, BENCH_SCAN_FUSED, zoh=w.zoh, h0=False)
+    G.say(G.compare(y[:, :, ds], y_ref, G.TOL["bf16"], "long fused y (sampled channels)"),
+          G.compare(hl[:, ds], h_ref, G.TOL["bf16"], "long fused h_last (sampled channels)"))
+
+
+def test_workload_decode_fused_sampled():
+    """512 consecutive ssm_step calls on (256, 5120, 16) with the fused steps
+    of the decode bench run (softplus step size with bias, output gate, a
+    4-tap conv over the rolling window), state and window updated in place;
+    sampled channels checked token by token against the oracle's decode step,
+    the window exactly."""
+    w = SI.WORKLOADS["decode"]
+    n = w.steps
+    inp = SI.decode_inputs(w)
+    ex = SI.fused_inputs(w.with_(conv_k=4), steps=n)
+    G.say("workload decode, fused", w)
+    h = G.dev(inp["h"])
+    A, Dv = G.dev(inp["A"]), G.dev(inp["D"])
+    xs, Bs, Cs = (G.dev(inp[k], "bf16") for k in ("x", "B", "C"))
+    drs, zs = G.dev(ex["delta_raw"], "bf16"), G.dev(ex["z"], "bf16")
+    bias, cw, cb = G.dev(ex["delta_bias"]), G.dev(ex["conv_w"]), G.dev(ex["conv_b"])
+    cs = G.dev(ex["conv_state"])
+    ys = torch.empty((n, w.batch, w.dim), dtype=torch.bfloat16, device="cuda")
+    for s in range(n):
+        ssm.step(h, xs[s], drs[s], A, Bs[s], Cs[s], Dv, y=ys[s], delta_bias=bias,
+                 delta_softplus=True, z=zs[s], conv_w=cw, conv_b=cb, conv_state=cs)
+    torch.cuda.synchronize()
+    y, h_fin, cs_fin = G.host(ys), h.cpu().numpy(), cs.cpu().numpy()
+    orc = oracle.default()
+    tol = G.TOL["bf16"]
+    rng = np.random.default_rng(8)
+    for b in [0, 1, 255] + list(rng.integers(0, w.batch, 2)):
+        ds = sorted(set([0, 63, 64, 5119] + list(rng.integers(0, w.dim, 4))))
+        sl = lambda a: np.ascontiguousarray(a[b:b + 1][:, ds])
+        hr = sl(inp["h"]).astype(np.float64)
+        csr = sl(ex["conv_state"]).astype(np.float64)
+        for s in range(n):
+            yr, hr, csr = orc.step(hr, sl(inp["x"][s]), sl(ex["delta_raw"][s]), inp["A"][ds],
+                                   inp["B"][s][b:b + 1], inp["C"][s][b:b + 1], inp["D"][ds],
+                                   delta_bias=ex["delta_bias"][ds], delta_softplus=True,
+                                   z=sl(ex["z"][s]), conv_w=ex["conv_w"][ds],
+                                   conv_b=ex["conv_b"][ds], conv_state=csr)
+            G.compare(y[s][b:b + 1][:, ds], yr, tol, "fused decode y step %d b=%d" % (s, b))
+        G.compare(sl(h_fin), hr, tol, "fused decode h b=%d" % b)
+        assert np.array_equal(sl(cs_fin), csr.astype(np.float32)), "fused decode window b=%d" % b
