@@ -129,8 +129,9 @@ def test_bwd_empty_sequence():
 def test_bwd_workload_fp32_full():
     """The bench's backward at full size (batch 8, L 2048, D 1536, N 16,
     fp32): the same seeded inputs and upstream gradients, the forward keeping
-    its states and the backward started from them, every gradient compared
-    with the oracle element by element."""
+    its states and the backward started from them, and the backward that
+    computes the states itself; every gradient of both compared with the
+    oracle element by element."""
     w = SI.WORKLOADS["fp32"]
     G.say("workload", w)
     inp = SI.scan_inputs(w, h0=True)
@@ -142,14 +143,18 @@ def test_bwd_workload_fp32_full():
     fwd, _, _ = ssm.prepare_scan(t["x"], t["delta"], A, t["B"], t["C"], Dv, h0=h0, h_saved=hs)
     bwd, g = ssm.prepare_bwd(t["x"], t["delta"], A, t["B"], t["C"], dy, D=Dv, h0=h0,
                              dh_last=dhl, h_saved=hs)
+    own, g_own = ssm.prepare_bwd(t["x"], t["delta"], A, t["B"], t["C"], dy, D=Dv, h0=h0,
+                                 dh_last=dhl)
     fwd.run()
     bwd.run()
+    own.run()
     torch.cuda.synchronize()
     ref = oracle.default().scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
                                     gi["dy"], D=inp["D"], h0=inp["h0"], dh_last=gi["dh_last"],
                                     nthreads=G.threads())
     for k in GRADS:
         G.say(compare_grad(g[k].cpu().numpy(), ref[k], "f32", k))
+        G.say(compare_grad(g_own[k].cpu().numpy(), ref[k], "f32", k + " (states recomputed)"))
 
 
 def test_bwd_workload_long_sampled():
