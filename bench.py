@@ -411,8 +411,8 @@ def main():
                          "its FETCH_SIZE / WRITE_SIZE counters calibrate HBM traffic")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the scan is not sharded across GPUs in this "
-              "library (see the design notes); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the scan is not sharded across GPUs by this "
+              "library; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

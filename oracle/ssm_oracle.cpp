@@ -55,7 +55,7 @@
 // Evaluation" and VMamba note, section "硬件感知的设计" -- but print no
 // gradient formula; the derivative of the defined function is the reading.)
 //
-// Readings where the pages are silent (listed in the design notes too):
+// Readings where the pages are silent:
 //   - the initial state h0 precedes token 0, so y_0 already contains x_0;
 //   - Abar at step t uses Delta_t, the same step as x_t;
 //   - with ZOH and A[d,n] == 0 the input factor is the limit Delta;
