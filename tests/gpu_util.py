@@ -1,6 +1,6 @@
 """Helpers of the GPU parity tests: moving seeded inputs to the device, calling
-the library through its binding, and comparing with the oracle at the
-tolerances the benchmark spec fixes (numpy allclose convention |got - ref| <= atol +
+the library through its binding, and comparing with the oracle at these
+tolerances (numpy allclose convention |got - ref| <= atol +
 rtol |ref|):
   fp32 inputs:                   rtol 2e-4, atol 1e-5
   bf16 inputs with fp32 state:   rtol 2e-2, atol 1e-3

@@ -406,7 +406,7 @@ def pin_decode_equals_scan(orc):
 
 # --------------------------------------------------------------------------
 # P9: causal depthwise conv1d + SiLU prologue (p2 SelectiveSSM: Conv1d with
-#     padding d_conv - 1 and groups = d_model, causal; SiLU per the task text)
+#     padding d_conv - 1 and groups = d_model, causal; SiLU z * sigmoid(z))
 # --------------------------------------------------------------------------
 
 def _conv_only(orc, x, w, bias):
