@@ -67,7 +67,11 @@
  *              library allocates nothing, keeps no pointer after the call and
  *              holds no global mutable state; it is reentrant and thread-safe.
  *   Streams    hip_stream is a hipStream_t (NULL = the default stream).  Work
- *              is enqueued asynchronously; the call never synchronizes.
+ *              is enqueued asynchronously; the call never synchronizes.  A
+ *              call enqueues kernel launches only (plus the optional timing
+ *              events), with no memset or copy, so it may be recorded by
+ *              stream capture into a HIP graph and replayed; a replay reads
+ *              the buffers whose addresses were passed when it was captured.
  *   Errors     all argument checks run on the host before anything is
  *              enqueued; on any error the outputs are untouched and the
  *              status says why (ssm_last_error_message() has the detail).  A
