@@ -386,7 +386,30 @@ def cpu_baseline(w, inp, budget_s=20.0, min_s=10.0):
     return {"value": (rows + (passes - 1) * w.batch) * elems / dt, "unit": "elem/s",
             "cores": cores, "kind": "oracle",
             "sample": "%s (%d x %d x %d elems each), fp64 sequential recurrence, %.1f s wall"
-                      % (what, w.seqlen, w.dim, w.dstate, dt)}
+                      % (what, w.seqlen, w.dim, w.dstate, dt),
+            "single_thread": cpu_single_thread(w, inp, orc)}
+
+
+def cpu_single_thread(w, inp, orc, min_s=1.0):
+    """The same oracle on one thread over 1/64 of the channels of one batch
+    row (whole passes repeated until min_s has elapsed): a per-core figure
+    beside the all-cores baseline."""
+    import numpy as np
+    nd = max(1, w.dim // 64)
+    part = {k: np.ascontiguousarray(inp[k][:1, :, :nd]) for k in ("x", "delta")}
+    for k in ("A", "D", "conv_w", "conv_b"):
+        part[k] = None if inp.get(k) is None else np.ascontiguousarray(inp[k][:nd])
+    dt, passes = 0.0, 0
+    while dt < min_s:
+        t = time.perf_counter()
+        orc.scan(part["x"], part["delta"], part["A"], inp["B"][:1], inp["C"][:1], part["D"],
+                 conv_w=part["conv_w"], conv_b=part["conv_b"], zoh=w.zoh, want_h_last=False,
+                 nthreads=1)
+        dt += time.perf_counter() - t
+        passes += 1
+    return {"value": passes * w.seqlen * nd * w.dstate / dt, "unit": "elem/s",
+            "sample": "%d passes over %d channels of one batch row, one thread, %.1f s wall"
+                      % (passes, nd, dt)}
 
 
 def main():
