@@ -304,7 +304,19 @@ def bench_decode(w, steps, warmup, torch, ssm, fused=False):
     # the average launch duration, inter-launch gap included; events around
     # each launch would add their own overhead to every launch instead.
     launch_us = e0.elapsed_time(e1) * 1e3 / (steps * n)
-    return dict(total_ms=e0.elapsed_time(e1), wall_s=wall, launch_us=launch_us)
+    # one more decode of all the tokens right after a 1 GiB write that evicts
+    # L2 and the Infinity Cache (state and inputs start in HBM)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush.fill_(1)
+    f0 = torch.cuda.Event(enable_timing=True)
+    f1 = torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    run()
+    f1.record(stream)
+    torch.cuda.synchronize()
+    del flush
+    return dict(total_ms=e0.elapsed_time(e1), wall_s=wall, launch_us=launch_us,
+                flushed_ms=f0.elapsed_time(f1), inp=inp)
 
 
 def bench_bwd(w, steps, warmup, torch, ssm, kept=True, train=False):
@@ -388,6 +400,30 @@ def cpu_baseline(w, inp, budget_s=20.0, min_s=10.0):
             "sample": "%s (%d x %d x %d elems each), fp64 sequential recurrence, %.1f s wall"
                       % (what, w.seqlen, w.dim, w.dstate, dt),
             "single_thread": cpu_single_thread(w, inp, orc)}
+
+
+def cpu_baseline_decode(w, inp, min_s=10.0):
+    """The oracle's decode step on this host's cores over the workload's
+    tokens in order (whole passes over all of them repeated until min_s has
+    elapsed)."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    orc = oracle.default()
+    dt, tokens = 0.0, 0
+    while dt < min_s:
+        h = inp["h"]
+        for s in range(w.steps):
+            t = time.perf_counter()
+            _, h = orc.step(h, inp["x"][s], inp["delta"][s], inp["A"], inp["B"][s],
+                            inp["C"][s], inp["D"], nthreads=cores)
+            dt += time.perf_counter() - t
+            tokens += 1
+            if dt >= min_s and tokens >= 8:
+                break
+    per_token = w.batch * w.dim * w.dstate
+    return {"value": tokens * per_token / dt, "unit": "elem/s", "cores": cores, "kind": "oracle",
+            "sample": "%d decode steps of %d x %d x %d elems in order, fp64, %.1f s wall"
+                      % (tokens, w.batch, w.dim, w.dstate, dt)}
 
 
 def cpu_single_thread(w, inp, orc, min_s=1.0):
@@ -486,7 +522,10 @@ def main():
                           "in_dtype": w.in_dtype, "state": "f32",
                           "fused": "softplus+gate+conv4" if args.fused else None},
                "hbm_gbps": bytes_ / (ms * 1e-3) / 1e9,
-               "roofline": roof, "cpu_baseline": None}
+               "flushed_ms_per_step": r["flushed_ms"],
+               "roofline": roof,
+               "cpu_baseline": (None if args.no_cpu_baseline or args.fused
+                                else cpu_baseline_decode(w, r["inp"]))}
         print(json.dumps(out), flush=True)
         return
 
