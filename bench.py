@@ -359,7 +359,7 @@ def bench_bwd(w, steps, warmup, torch, ssm, kept=True, train=False):
     main_ms = [hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)]
     hip.destroy(evs)
     return dict(total_ms=e0.elapsed_time(e1), main_ms=main_ms,
-                super_chunk=None)
+                super_chunk=None, inp=inp, gi=gi)
 
 
 def cpu_baseline(w, inp, budget_s=20.0, min_s=10.0):
@@ -400,6 +400,45 @@ def cpu_baseline(w, inp, budget_s=20.0, min_s=10.0):
             "sample": "%s (%d x %d x %d elems each), fp64 sequential recurrence, %.1f s wall"
                       % (what, w.seqlen, w.dim, w.dstate, dt),
             "single_thread": cpu_single_thread(w, inp, orc)}
+
+
+def cpu_baseline_bwd(w, inp, gi, train, budget_s=20.0, min_s=10.0):
+    """The oracle's backward (after its forward when `train`) on this host's
+    cores: whole batch rows of the same workload, as many as fit the budget
+    (at least one), whole passes repeated until min_s has elapsed."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    orc = oracle.default()
+
+    def run(lo, hi):
+        t = time.perf_counter()
+        if train:
+            orc.scan(inp["x"][lo:hi], inp["delta"][lo:hi], inp["A"], inp["B"][lo:hi],
+                     inp["C"][lo:hi], inp["D"], h0=inp["h0"][lo:hi], zoh=w.zoh,
+                     nthreads=cores)
+        orc.scan_bwd(inp["x"][lo:hi], inp["delta"][lo:hi], inp["A"], inp["B"][lo:hi],
+                     inp["C"][lo:hi], gi["dy"][lo:hi], D=inp["D"], h0=inp["h0"][lo:hi],
+                     dh_last=gi["dh_last"][lo:hi], zoh=w.zoh, nthreads=cores)
+        return time.perf_counter() - t
+
+    dt = run(0, 1)
+    rows = 1
+    extra = int(min(w.batch - 1, max(0, budget_s / max(dt, 1e-6) - 1)))
+    if extra > 0:
+        dt += run(1, 1 + extra)
+        rows += extra
+    passes = 1
+    if rows == w.batch:
+        while dt < min_s:
+            dt += run(0, w.batch)
+            passes += 1
+    what = ("%d passes over all %d batch rows" % (passes, w.batch) if passes > 1
+            else "%d of %d batch rows" % (rows, w.batch))
+    return {"value": (rows + (passes - 1) * w.batch) * w.seqlen * w.dim * w.dstate / dt,
+            "unit": "elem/s", "cores": cores, "kind": "oracle",
+            "sample": "%s (%d x %d x %d elems each), fp64 %s, %.1f s wall"
+                      % (what, w.seqlen, w.dim, w.dstate,
+                         "forward + reverse sweep" if train else "reverse-mode sweep", dt)}
 
 
 def cpu_baseline_decode(w, inp, min_s=10.0):
@@ -552,7 +591,9 @@ def main():
                           "batch": w.batch,
                           "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
                           "in_dtype": w.in_dtype, "disc": "zoh" if w.zoh else "delta_b"},
-               "roofline": roof, "cpu_baseline": None}
+               "roofline": roof,
+               "cpu_baseline": (None if args.no_cpu_baseline
+                                else cpu_baseline_bwd(w, r["inp"], r["gi"], args.train))}
         print(json.dumps(out), flush=True)
         return
 
