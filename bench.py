@@ -120,6 +120,20 @@ def algorithmic_bytes(w, h0=False, h_last=False, fused=False) -> int:
     return n
 
 
+def decode_bytes(w, fused=False) -> int:
+    """Algorithmic bytes of one decode step: h read and written (fp32), x,
+    Delta and y, the B and C rows, A and D; fused also z, delta_bias, the conv
+    weights and bias and the fp32 window read and written."""
+    s_in = 2 if w.in_dtype == "bf16" else 4
+    n = (2 * 4 * w.batch * w.dim * w.dstate + w.batch * w.dim * 3 * s_in
+         + 2 * w.batch * w.dstate * s_in + 4 * w.dim * (w.dstate + 1))
+    if fused:
+        K = FUSED_DECODE_CONV_K
+        n += (w.batch * w.dim * s_in + 4 * w.dim * (2 + K)
+              + 2 * 4 * w.batch * w.dim * (K - 1))
+    return n
+
+
 # VALU lane-slots per (b, t, d) of the fused steps: softplus (bias add, scale,
 # exp (2), 1 + e, compare + select, log (2), 2 muls, sub, rcp (2)) and the
 # gate (scale, exp (2), add, rcp (2), 2 muls)
@@ -535,15 +549,7 @@ def main():
         r = bench_decode(w, args.steps, args.warmup, torch, ssm, fused=args.fused)
         ms = r["total_ms"] / args.steps
         elems = w.elems
-        # per token: h read + written (fp32), x, Delta, y (bf16), B, C rows
-        s_in = 2 if w.in_dtype == "bf16" else 4
-        per_launch = (2 * 4 * w.batch * w.dim * w.dstate + w.batch * w.dim * 3 * s_in
-                      + 2 * w.batch * w.dstate * s_in + 4 * w.dim * (w.dstate + 1))
-        if args.fused:
-            # z, delta_bias, conv weights and bias, the fp32 window read and written
-            K = FUSED_DECODE_CONV_K
-            per_launch += (w.batch * w.dim * s_in + 4 * w.dim * (2 + K)
-                           + 2 * 4 * w.batch * w.dim * (K - 1))
+        per_launch = decode_bytes(w, fused=args.fused)
         bytes_ = w.steps * per_launch
         ach = per_launch / (r["launch_us"] * 1e-6) / 1e9
         copy = copy_bandwidth(torch)
