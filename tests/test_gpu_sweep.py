@@ -1,0 +1,198 @@
+"""Seeded sweeps over drawn configurations, each compared element by element
+with the oracle; the draws are fixed, so every run checks the same cases.
+
+  forward: batch 1-4, lengths 1-700 (ragged tails, lengths below one block),
+           1-200 channels (ragged tiles), every supported N, both dtypes in
+           and out, both discretizations, conv taps 0-4 with or without a
+           carried window, h0 or not, the library's chunk plan or a forced
+           chunk length (down to 1), any mix of the fused steps;
+  decode:  three consecutive steps, batch 1-300, 1-300 channels, every N,
+           dtypes, discretizations, conv taps 0-4 with the window in place,
+           step-size transform and gate;
+  backward: batch 1-3, lengths 1-300, 1-130 channels, every N, both dtypes,
+           both discretizations, h0, dh_last and the skip weight or not, a
+           forced super-chunk or the plan, the forward's kept states or not
+           (gradients compared as in the backward tests)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import gpu_util as G
+import ssm_inputs as SI
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+import selective_state_space_83_amd as ssm  # noqa: E402
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _lib():
+    ssm.load_library()
+    yield
+
+
+def _draw(i):
+    rng = np.random.default_rng(8300 + i)
+    Bt = int(rng.integers(1, 5))
+    L = int(rng.choice([1, 2, 3, 5, 16, 17, 63, 100, 257, 511, 700]))
+    D = int(rng.choice([1, 3, 31, 64, 65, 127, 130, 200]))
+    N = int(rng.choice([1, 2, 4, 8, 16]))
+    idt = str(rng.choice(["f32", "bf16"]))
+    odt = str(rng.choice(["f32", "bf16"]))
+    zoh = bool(rng.integers(0, 2))
+    K = int(rng.choice([0, 0, 1, 2, 3, 4]))
+    h0 = bool(rng.integers(0, 2))
+    cl = int(rng.choice([0, 0, 1, 4, 7, 32, 100]))
+    use = set()
+    dt = int(rng.integers(0, 3))
+    if dt == 1:
+        use.add("bias")
+    elif dt == 2:
+        use.add("softplus")
+    if rng.integers(0, 2):
+        use.add("gate")
+    if K and rng.integers(0, 2):
+        use.add("state")
+    return Bt, L, D, N, idt, odt, zoh, K, h0, cl, frozenset(use)
+
+
+CASES = [_draw(i) for i in range(48)]
+
+
+def _id(c):
+    return "b%d_L%d_D%d_N%d_%s_%s_zoh%d_k%d_h%d_cl%d_%s" % (
+        c[:10] + ("+".join(sorted(c[10])) or "plain",))
+
+
+@pytest.mark.parametrize("case", CASES, ids=_id)
+def test_sweep(case):
+    Bt, L, D, N, idt, odt, zoh, K, h0, cl, use = case
+    G.say("case", case)
+    w = SI.Workload("sweep", 300 + CASES.index(case), Bt, L, D, N, idt, odt, zoh=zoh, conv_k=K,
+                    a_dist="random", dskip_dist="uniform")
+    inp = SI.scan_inputs(w, h0=h0)
+    ex = SI.fused_inputs(w)
+    y, hl, cs = G.gpu_scan_fused(inp, ex, use, idt, odt, zoh=zoh, chunk_len=cl, h0=h0)
+    y_ref, h_ref, cs_ref = G.oracle_scan_fused(inp, ex, use, zoh=zoh, h0=h0)
+    G.compare(y, y_ref, G.y_tol(idt, odt), "y")
+    G.compare(hl, h_ref, G.TOL[idt], "h_last")
+    if cs_ref is not None:
+        assert np.array_equal(cs, cs_ref.astype(np.float32)), "conv window"
+
+
+def _draw_step(i):
+    rng = np.random.default_rng(8400 + i)
+    Bt = int(rng.choice([1, 2, 7, 64, 300]))
+    D = int(rng.choice([1, 5, 16, 63, 64, 65, 300]))
+    N = int(rng.choice([1, 2, 4, 8, 16]))
+    idt = str(rng.choice(["f32", "bf16"]))
+    odt = str(rng.choice(["f32", "bf16"]))
+    zoh = bool(rng.integers(0, 2))
+    K = int(rng.choice([0, 0, 1, 2, 3, 4]))
+    use = set()
+    dt = int(rng.integers(0, 3))
+    if dt == 1:
+        use.add("bias")
+    elif dt == 2:
+        use.add("softplus")
+    if rng.integers(0, 2):
+        use.add("gate")
+    return Bt, D, N, idt, odt, zoh, K, frozenset(use)
+
+
+STEP_CASES = [_draw_step(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "b%d_D%d_N%d_%s_%s_zoh%d_k%d_%s" % (
+    c[:7] + ("+".join(sorted(c[7])) or "plain",)))
+def test_sweep_step(case):
+    Bt, D, N, idt, odt, zoh, K, use = case
+    G.say("case", case)
+    steps = 3
+    w = SI.Workload("sweepstep", 400 + STEP_CASES.index(case), Bt, 1, D, N, idt, odt, zoh=zoh,
+                    conv_k=K, a_dist="random", dskip_dist="uniform")
+    inp = SI.scan_inputs(w.with_(seqlen=steps), h0=True)
+    ex = SI.fused_inputs(w, steps=steps)
+    ex_t = dict(ex, delta_raw=ex["delta_raw"].transpose(1, 0, 2))
+    dls, bias, sp = G.step_size_inputs(inp, ex_t, use)
+    h = G.dev(inp["h0"])
+    hr = inp["h0"].astype(np.float64)
+    A, Dv = G.dev(inp["A"]), G.dev(inp["D"])
+    cw = G.dev(inp["conv_w"]) if K else None
+    cb = G.dev(inp["conv_b"]) if K else None
+    cs = G.dev(ex["conv_state"]) if K else None
+    csr = ex["conv_state"].astype(np.float64) if K else None
+    orc = oracle.default()
+    for t in range(steps):
+        dl = np.ascontiguousarray(dls[:, t])
+        z = ex["z"][t] if "gate" in use else None
+        yt = ssm.step(h, G.dev(np.ascontiguousarray(inp["x"][:, t]), idt), G.dev(dl, idt), A,
+                      G.dev(np.ascontiguousarray(inp["B"][:, t]), idt),
+                      G.dev(np.ascontiguousarray(inp["C"][:, t]), idt), Dv, zoh=zoh,
+                      out_dtype=G.torch_dtype(odt), delta_bias=G.dev(bias), delta_softplus=sp,
+                      z=G.dev(z, idt), conv_w=cw, conv_b=cb, conv_state=cs)
+        res = orc.step(hr, inp["x"][:, t], dl, inp["A"], inp["B"][:, t], inp["C"][:, t],
+                       inp["D"], zoh=zoh, delta_bias=bias, delta_softplus=sp, z=z,
+                       conv_w=inp["conv_w"] if K else None, conv_b=inp["conv_b"] if K else None,
+                       conv_state=csr)
+        yr, hr = res[0], res[1]
+        if K:
+            csr = res[2]
+        G.compare(G.host(yt), yr, G.y_tol(idt, odt), "step %d y" % t)
+        G.compare(h.cpu().numpy(), hr, G.TOL[idt], "step %d h" % t)
+        if K:
+            assert np.array_equal(cs.cpu().numpy(), csr.astype(np.float32)), "step %d window" % t
+
+
+def _draw_bwd(i):
+    rng = np.random.default_rng(8500 + i)
+    Bt = int(rng.integers(1, 4))
+    L = int(rng.choice([1, 2, 15, 16, 17, 33, 100, 300]))
+    D = int(rng.choice([1, 7, 64, 65, 130]))
+    N = int(rng.choice([1, 2, 4, 8, 16]))
+    idt = str(rng.choice(["f32", "bf16"]))
+    zoh = bool(rng.integers(0, 2))
+    flags = [bool(v) for v in rng.integers(0, 2, 3)]   # h0, dh_last, skip
+    sc = int(rng.choice([0, 0, 16, 32, 64]))
+    kept = bool(rng.integers(0, 2))
+    return (Bt, L, D, N, idt, zoh) + tuple(flags) + (sc, kept)
+
+
+BWD_CASES = [_draw_bwd(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "b%d_L%d_D%d_N%d_%s_zoh%d_h%d_g%d_s%d_sc%d_kept%d" % c)
+def test_sweep_bwd(case):
+    Bt, L, D, N, idt, zoh, h0, dhl, skip, sc, kept = case
+    G.say("case", case)
+    w = SI.Workload("sweepbwd", 500 + BWD_CASES.index(case), Bt, L, D, N, idt, idt, zoh=zoh,
+                    a_dist="random", dskip_dist="uniform")
+    inp = SI.scan_inputs(w, h0=h0)
+    gi = SI.grad_inputs(w)
+    dh_last = gi["dh_last"] if dhl else None
+    Dv = inp["D"] if skip else None
+    t = {k: G.dev(inp[k], idt) for k in ("x", "delta", "B", "C")}
+    A, h0d = G.dev(inp["A"]), G.dev(inp.get("h0"))
+    hs = None
+    if kept:
+        hs = torch.empty(ssm.saved_states_shape(Bt, L, D, N), device="cuda")
+        ssm.scan(t["x"], t["delta"], A, t["B"], t["C"], G.dev(Dv), h0=h0d, zoh=zoh, h_saved=hs)
+    g = ssm.scan_bwd(t["x"], t["delta"], A, t["B"], t["C"], G.dev(gi["dy"], idt), D=G.dev(Dv),
+                     h0=h0d, dh_last=G.dev(dh_last), zoh=zoh, super_chunk=sc, h_saved=hs)
+    torch.cuda.synchronize()
+    ref = oracle.default().scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                                    gi["dy"], D=Dv, h0=inp.get("h0"), dh_last=dh_last, zoh=zoh,
+                                    nthreads=G.threads())
+    r = 2e-4 if idt == "f32" else 2e-2
+    for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dh0"):
+        if k not in g or ref.get(k) is None:
+            continue
+        want = np.asarray(ref[k], dtype=np.float64)
+        scale = float(np.abs(want).max()) if want.size else 0.0
+        G.compare(g[k].cpu().numpy(), want, dict(rtol=r, atol=r * scale + 1e-30), k)
