@@ -125,10 +125,17 @@ def test_workload_long_lti_closed_form():
     y, _ = G.gpu_scan(inp, w.in_dtype, w.out_dtype, h0=False, want_h_last=False)
     L = w.seqlen
     rng = np.random.default_rng(6)
-    ts = sorted(set([0, 1, 2, 63, 64, 2047, 2048, 65535, L - 2, L - 1]
-                    + list(rng.integers(0, L, 12))))
+    # 64 sampled steps (start, chunk edges, end, random) x 16 sampled channels
+    # (the sizes the LTI pin of the workload recipe asks for)
+    fixed = [0, 1, 2, 63, 64, 2047, 2048, 65535, L - 2, L - 1]
+    pool = np.setdiff1d(np.arange(3, L - 2), fixed)
+    ts = sorted(fixed + [int(t) for t in rng.choice(pool, 64 - len(fixed), replace=False)])
+    fixed_d = [0, 7, 200, 511]
+    pool_d = np.setdiff1d(np.arange(1, 511), fixed_d)
+    chans = sorted(fixed_d + [int(v) for v in rng.choice(pool_d, 12, replace=False)])
+    assert len(set(ts)) == 64 and len(set(chans)) == 16
     tol = G.TOL["bf16"]
-    for d in [0, 7, 200, 511]:
+    for d in chans:
         dt = float(inp["delta"][0, 0, d])
         A = inp["A"][d].astype(np.float64)
         Bv = inp["B"][0, 0].astype(np.float64)
