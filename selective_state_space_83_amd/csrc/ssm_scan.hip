@@ -835,7 +835,12 @@ ssm_status_t ssm_scan_bwd(const ssm_scan_bwd_args_t* a, void* hip_stream) {
 }
 
 const char* ssm_status_string(ssm_status_t s) {
-  switch (s) {
+  // Any integer may arrive here; an enum object holding a value outside its
+  // enumerators' range must not be read as the enum, so read its bits.
+  static_assert(sizeof(s) == sizeof(int), "ssm_status_t is int-sized");
+  int v;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case SSM_OK: return "ok";
     case SSM_ERR_NULL: return "required pointer is NULL";
     case SSM_ERR_SHAPE: return "invalid or overflowing sizes";

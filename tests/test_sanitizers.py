@@ -1,0 +1,149 @@
+"""CPU runs under AddressSanitizer and UndefinedBehaviorSanitizer.
+
+  * the oracle, rebuilt with -fsanitize=address,undefined, runs forward scans
+    (conv prologue, fused steps, ZOH, h0 and h_last), decode steps with a conv
+    window and backward sweeps on small odd shapes;
+  * the HIP library's host code (argument checks, plans, workspace queries),
+    rebuilt from the same sources with the sanitizers on its host pass (its
+    device pass unoptimized: nothing is launched), runs every ABI-level query
+    and rejected call the CPU can make without a device.
+
+Each run is a child process with the sanitizer runtime preloaded; any report
+ends it with a non-zero status."""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+import textwrap
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ENV_SAN = {"ASAN_OPTIONS": "detect_leaks=0:abort_on_error=1",
+           "UBSAN_OPTIONS": "halt_on_error=1:print_stacktrace=1"}
+
+
+def _run(script, preload, timeout=600):
+    env = dict(os.environ, LD_PRELOAD=preload, **ENV_SAN)
+    r = subprocess.run([sys.executable, "-c", textwrap.dedent(script)], env=env,
+                       capture_output=True, text=True, timeout=timeout)
+    assert r.returncode == 0 and "ok" in r.stdout, (r.returncode, r.stdout[-2000:],
+                                                    r.stderr[-4000:])
+
+
+def test_oracle_under_sanitizers(tmp_path):
+    lib = str(tmp_path / "libssm_oracle_san.so")
+    subprocess.run(["g++", "-O1", "-g", "-std=c++17", "-shared", "-fPIC", "-pthread",
+                    "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                    "-fno-omit-frame-pointer", os.path.join(ROOT, "oracle", "ssm_oracle.cpp"),
+                    "-o", lib], check=True)
+    asan = subprocess.run(["g++", "-print-file-name=libasan.so"], capture_output=True,
+                          text=True).stdout.strip()
+    ubsan = subprocess.run(["g++", "-print-file-name=libubsan.so"], capture_output=True,
+                           text=True).stdout.strip()
+    _run(f"""
+        import sys
+        import numpy as np
+        sys.path.insert(0, {ROOT!r})
+        import oracle
+        import ssm_inputs as SI
+        orc = oracle.Oracle({lib!r})
+        for i, (Bt, L, D, N, K, zoh) in enumerate([(2, 37, 5, 3, 4, True), (1, 1, 1, 1, 0, False),
+                                                   (3, 19, 7, 16, 2, False)]):
+            w = SI.Workload("san", 600 + i, Bt, L, D, N, "f32", "f32", zoh=zoh, conv_k=K,
+                            a_dist="random", dskip_dist="uniform")
+            inp = SI.scan_inputs(w, h0=True)
+            ex = SI.fused_inputs(w)
+            cs_out = np.zeros((Bt, D, max(K - 1, 0)))
+            kw = dict(conv_state_in=ex["conv_state"], conv_state_out=cs_out) if K > 1 else {{}}
+            y, h = orc.scan(inp["x"], ex["delta_raw"], inp["A"], inp["B"], inp["C"], inp["D"],
+                            h0=inp["h0"], conv_w=inp["conv_w"], conv_b=inp["conv_b"], zoh=zoh,
+                            delta_bias=ex["delta_bias"], delta_softplus=True, z=ex["z"],
+                            nthreads=3, **kw)
+            assert np.all(np.isfinite(y)) and np.all(np.isfinite(h))
+            ys = orc.step(inp["h0"], inp["x"][:, 0], inp["delta"][:, 0], inp["A"], inp["B"][:, 0],
+                          inp["C"][:, 0], inp["D"], zoh=zoh, z=ex["z"][:, 0],
+                          conv_w=inp["conv_w"], conv_b=inp["conv_b"],
+                          conv_state=ex["conv_state"] if K else None)
+            assert np.all(np.isfinite(ys[0]))
+            gi = SI.grad_inputs(w)
+            g = orc.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], gi["dy"],
+                             D=inp["D"], h0=inp["h0"], dh_last=gi["dh_last"], zoh=zoh, nthreads=2)
+            assert all(np.all(np.isfinite(v)) for v in g.values() if v is not None)
+        print("ok")
+        """, f"{asan} {ubsan}")
+
+
+def _sanitized_library():
+    """The library rebuilt with the sanitizers on its host pass (its device
+    pass at -O1: nothing is launched).  The build takes minutes, so it is kept
+    under a name derived from the sources and flags and reused while they are
+    unchanged."""
+    import hashlib
+    sys.path.insert(0, ROOT)
+    from selective_state_space_83_amd import _build as B
+    flags = (B.HIPCC_FLAGS +
+             ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+              "-fsanitize=undefined", "-Xarch_host", "-fno-sanitize-recover=undefined",
+              "-shared-libsan", "-Xarch_device", "-O1"])
+    h = hashlib.sha256(" ".join(flags).encode())
+    for src in sorted(glob.glob(os.path.join(B.CSRC, "*"))) + [os.path.join(B.INCLUDE, "ssm_scan.h")]:
+        h.update(open(src, "rb").read())
+    out_dir = os.path.join(B.HERE, "_san")
+    os.makedirs(out_dir, exist_ok=True)
+    lib = os.path.join(out_dir, "libssmscan_san_%s.so" % h.hexdigest()[:16])
+    if not os.path.exists(lib):
+        for old in glob.glob(os.path.join(out_dir, "libssmscan_san_*.so")):
+            os.remove(old)
+        tmp = lib + ".tmp%d" % os.getpid()
+        r = subprocess.run([B.hipcc()] + flags + B.SOURCES + ["-o", tmp], capture_output=True,
+                           text=True)
+        assert r.returncode == 0, r.stderr[-3000:]
+        os.replace(tmp, lib)
+    return lib
+
+
+def test_library_host_code_under_sanitizers():
+    rt = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not rt:
+        pytest.skip("no clang AddressSanitizer runtime in this image")
+    lib = _sanitized_library()
+    _run(f"""
+        import ctypes, sys
+        sys.path.insert(0, {ROOT!r})
+        sys.path.insert(0, {os.path.join(ROOT, "tests")!r})
+        import selective_state_space_83_amd as ssm
+        lib = ssm.load_library({lib!r})
+        assert lib.ssm_abi_version() == ssm.ABI_VERSION
+        for code in range(-1, 10):
+            lib.ssm_status_string(code)
+        # plans and workspace sizes over shapes, chunk lengths and options
+        for (b, L, D, N) in [(2, 64, 32, 16), (8, 2048, 1536, 16), (1, 1 << 20, 512, 16),
+                             (3, 1000, 65, 4), (1, 1, 1, 1), (0, 5, 3, 2), (2, 0, 3, 2)]:
+            for cl in (0, 1, 7, 100):
+                a = ssm.ScanArgs()
+                a.batch, a.seqlen, a.dim, a.dstate, a.chunk_len = b, L, D, N, cl
+                lib.ssm_scan_workspace_size(ctypes.byref(a))
+                lib.ssm_scan_plan_chunk_len(ctypes.byref(a))
+                g = ssm.BwdArgs()
+                g.batch, g.seqlen, g.dim, g.dstate = b, L, D, N
+                lib.ssm_scan_bwd_workspace_size(ctypes.byref(g))
+        # calls rejected on the host before any launch
+        assert lib.ssm_scan_fwd(None, None) != 0
+        assert lib.ssm_step(None, None) != 0
+        assert lib.ssm_scan_bwd(None, None) != 0
+        a = ssm.ScanArgs()
+        a.batch, a.seqlen, a.dim, a.dstate = 2, 10, 3, 5      # unsupported N
+        assert lib.ssm_scan_fwd(ctypes.byref(a), None) != 0
+        a.dstate, a.seqlen = 16, -1                           # negative size
+        assert lib.ssm_scan_fwd(ctypes.byref(a), None) != 0
+        a.seqlen, a.batch, a.dim = 1 << 40, 1 << 40, 1 << 20  # overflow
+        assert lib.ssm_scan_fwd(ctypes.byref(a), None) != 0
+        assert len(lib.ssm_last_error_message()) > 0
+        s = ssm.StepArgs()
+        s.batch, s.dim, s.dstate = 2, 3, 16
+        assert lib.ssm_step(ctypes.byref(s), None) != 0       # null pointers
+        print("ok")
+        """, rt[-1], timeout=900)
