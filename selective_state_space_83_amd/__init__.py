@@ -193,6 +193,12 @@ def _ptr(t) -> Optional[int]:
         raise ValueError("tensor must be on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
+    # the library launches on the current device (its stream): every tensor
+    # must live there
+    cur = _torch().cuda.current_device()
+    if t.device.index is not None and t.device.index != cur:
+        raise ValueError("tensor is on cuda:%d but the current device is cuda:%d"
+                         % (t.device.index, cur))
     return t.data_ptr()
 
 
