@@ -313,3 +313,83 @@ def test_workload_decode_fused_sampled():
             G.compare(y[s][b:b + 1][:, ds], yr, tol, "fused decode y step %d b=%d" % (s, b))
         G.compare(sl(h_fin), hr, tol, "fused decode h b=%d" % b)
         assert np.array_equal(sl(cs_fin), csr.astype(np.float32)), "fused decode window b=%d" % b
+
+
+def _canaried(shape, dtype, pad, canary):
+    n = int(np.prod(shape))
+    buf = torch.full((n + 2 * pad,), canary, dtype=dtype, device="cuda")
+    return buf, buf[pad:pad + n].view(*shape)
+
+
+def _canary_intact(buf, pad, canary):
+    c = torch.tensor(canary, dtype=buf.dtype, device="cuda")
+    return bool(torch.all(buf[:pad] == c)) and bool(torch.all(buf[-pad:] == c))
+
+
+def test_fused_scan_no_writes_outside_outputs():
+    """A chunked fused scan (ZOH, 4-tap conv with its window carried, softplus,
+    gate) with bf16 y, h_last and conv_state_out inside canary-filled buffers
+    (70 channels: a ragged tile); every canary stays, and the outputs match
+    the oracle."""
+    Bt, L, D, N, K = 3, 333, 70, 16, 4
+    w = SI.Workload("canf", 170, Bt, L, D, N, "bf16", "bf16", zoh=True, conv_k=K,
+                    a_dist="random", dskip_dist="uniform")
+    inp = SI.scan_inputs(w, h0=True)
+    ex = SI.fused_inputs(w)
+    pad = 4096
+    ybuf, y = _canaried((Bt, L, D), torch.bfloat16, pad, -7.0)
+    hbuf, hl = _canaried((Bt, D, N), torch.float32, pad, -12345.5)
+    cbuf, cs = _canaried((Bt, D, K - 1), torch.float32, pad, -12345.5)
+    t = {k: G.dev(inp[k], "bf16") for k in ("x", "B", "C")}
+    ssm.scan(t["x"], G.dev(ex["delta_raw"], "bf16"), G.dev(inp["A"]), t["B"], t["C"],
+             G.dev(inp["D"]), h0=G.dev(inp["h0"]), conv_w=G.dev(inp["conv_w"]),
+             conv_b=G.dev(inp["conv_b"]), zoh=True, y=y, h_last=hl, chunk_len=40,
+             delta_bias=G.dev(ex["delta_bias"]), delta_softplus=True,
+             z=G.dev(ex["z"], "bf16"), conv_state_in=G.dev(ex["conv_state"]),
+             conv_state_out=cs)
+    torch.cuda.synchronize()
+    assert _canary_intact(ybuf, pad, -7.0), "y"
+    assert _canary_intact(hbuf, pad, -12345.5), "h_last"
+    assert _canary_intact(cbuf, pad, -12345.5), "conv_state_out"
+    y_ref, h_ref, cs_ref = G.oracle_scan_fused(inp, ex, ALL, zoh=True, h0=True)
+    G.compare(G.host(y), y_ref, G.TOL["bf16"], "canary fused y")
+    G.compare(hl.cpu().numpy(), h_ref, G.TOL["bf16"], "canary fused h_last")
+    assert np.array_equal(cs.cpu().numpy(), cs_ref.astype(np.float32))
+
+
+def test_step_no_writes_outside_outputs():
+    """Fused decode steps (4-tap window in place, softplus, gate) with h, bf16 y
+    and the window inside canary-filled buffers; 5 batch rows (a wave's second
+    row falls past the batch) and 70 channels (a ragged tile)."""
+    Bt, D, N, K, steps = 5, 70, 16, 4, 3
+    w = SI.Workload("cans", 171, Bt, 1, D, N, "bf16", "bf16", conv_k=K, a_dist="random",
+                    dskip_dist="uniform")
+    inp = SI.scan_inputs(w.with_(seqlen=steps), h0=True)
+    ex = SI.fused_inputs(w, steps=steps)
+    pad = 4096
+    hbuf, h = _canaried((Bt, D, N), torch.float32, pad, -12345.5)
+    cbuf, cs = _canaried((Bt, D, K - 1), torch.float32, pad, -12345.5)
+    ybuf, y = _canaried((Bt, D), torch.bfloat16, pad, -7.0)
+    h.copy_(G.dev(inp["h0"]))
+    cs.copy_(G.dev(ex["conv_state"]))
+    hr = inp["h0"].astype(np.float64)
+    csr = ex["conv_state"].astype(np.float64)
+    orc = oracle.default()
+    for s in range(steps):
+        xs = np.ascontiguousarray(inp["x"][:, s])
+        ssm.step(h, G.dev(xs, "bf16"), G.dev(ex["delta_raw"][s], "bf16"), G.dev(inp["A"]),
+                 G.dev(np.ascontiguousarray(inp["B"][:, s]), "bf16"),
+                 G.dev(np.ascontiguousarray(inp["C"][:, s]), "bf16"), G.dev(inp["D"]), y=y,
+                 delta_bias=G.dev(ex["delta_bias"]), delta_softplus=True,
+                 z=G.dev(ex["z"][s], "bf16"), conv_w=G.dev(inp["conv_w"]),
+                 conv_b=G.dev(inp["conv_b"]), conv_state=cs)
+        torch.cuda.synchronize()
+        assert _canary_intact(hbuf, pad, -12345.5), "h step %d" % s
+        assert _canary_intact(cbuf, pad, -12345.5), "window step %d" % s
+        assert _canary_intact(ybuf, pad, -7.0), "y step %d" % s
+        yr, hr, csr = orc.step(hr, xs, ex["delta_raw"][s], inp["A"], inp["B"][:, s],
+                               inp["C"][:, s], inp["D"], delta_bias=ex["delta_bias"],
+                               delta_softplus=True, z=ex["z"][s], conv_w=inp["conv_w"],
+                               conv_b=inp["conv_b"], conv_state=csr)
+        G.compare(G.host(y), yr, G.TOL["bf16"], "canary step %d y" % s)
+        G.compare(h.cpu().numpy(), hr, G.TOL["bf16"], "canary step %d h" % s)
