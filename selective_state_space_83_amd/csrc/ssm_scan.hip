@@ -28,8 +28,12 @@ ssm_status_t fail(ssm_status_t s, const char* fmt, ...) {
 // for four waves per SIMD.  A chunked plan uses at most kTargetWaves waves in
 // the output pass (rounding the chunk count down, so no partial extra round
 // of waves forms a tail), and never cuts chunks shorter than kMinChunk steps.
+// Problems too small to fill the chip gain most from short chunks: one wave
+// walking a long chunk alone is latency-bound (measured: 1 x 256 x 64 x 16,
+// 68.7 us at 64-step chunks, 18.9 us at 8; 2 x 2048 x 64 x 16, 72.5 vs
+// 26.5 us; 4-step chunks lost again on the latter).
 constexpr int64_t kTargetWaves = 4096;
-constexpr int64_t kMinChunk = 64;
+constexpr int64_t kMinChunk = 8;
 constexpr int64_t kChunkAlign = 4;
 constexpr int64_t kMaxChunk = int64_t(1) << 30;   // kernels count steps in 32 bits
 // A chunk's rows of x / Delta / y are addressed through one buffer resource
