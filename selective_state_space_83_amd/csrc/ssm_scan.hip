@@ -32,7 +32,17 @@ ssm_status_t fail(ssm_status_t s, const char* fmt, ...) {
 // walking a long chunk alone is latency-bound (measured: 1 x 256 x 64 x 16,
 // 68.7 us at 64-step chunks, 18.9 us at 8; 2 x 2048 x 64 x 16, 72.5 vs
 // 26.5 us; 4-step chunks lost again on the latter).
+// Where four waves per SIMD would cut chunks shorter than kShortChunk steps,
+// the plan takes three per SIMD instead (kShortTargetWaves): each wave's
+// start (its carry, constants and first rows) is then paid by fewer, longer
+// chunks.  Measured on fp32 inputs: 4 x 2048 x 768 x 16, 28-step chunks
+// (3,552 waves) 63 us vs 32-step chunks (3,072 waves) 53 us; 8 x 4096 x
+// 384 x 16, 52 vs 64 steps, 93 vs 84 us.  At 64 steps and more, three and
+// four waves per SIMD measured the same or four better (the bench workloads
+// keep their plans).
 constexpr int64_t kTargetWaves = 4096;
+constexpr int64_t kShortTargetWaves = 3072;
+constexpr int64_t kShortChunk = 64;
 constexpr int64_t kMinChunk = 8;
 constexpr int64_t kChunkAlign = 4;
 constexpr int64_t kMaxChunk = int64_t(1) << 30;   // kernels count steps in 32 bits
@@ -104,8 +114,11 @@ Plan make_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t chunk_len) {
     T = std::min<int64_t>(chunk_len, L);
   } else {
     const int64_t waves = Bt * pl.dtiles;
-    int64_t C = kTargetWaves / waves;
-    C = std::max<int64_t>(1, std::min<int64_t>(C, L / kMinChunk));
+    auto chunks = [&](int64_t target) {
+      return std::max<int64_t>(1, std::min<int64_t>(target / waves, L / kMinChunk));
+    };
+    int64_t C = chunks(kTargetWaves);
+    if (C > 1 && (L + C - 1) / C < kShortChunk) C = chunks(kShortTargetWaves);
     T = (L + C - 1) / C;
     if (C > 1) T = (T + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
     T = std::min(T, L);

@@ -441,6 +441,22 @@ def test_plan_and_workspace(lib, shape):
     assert ws == expected_ws(b, L, D, N, T)
 
 
+@pytest.mark.parametrize("shape,T", [
+    ((8, 2048, 1536, 16), 100),      # 192 wave columns x 21 chunks = 4032 waves
+    ((4, 8192, 2560, 16), 328),      # 160 x 25 = 4000
+    ((1, 1 << 20, 512, 16), 2048),   # 8 x 512 = 4096
+    ((1, 16384, 1024, 16), 64),      # 64-step chunks at four waves per SIMD stay
+    ((4, 2048, 768, 16), 32),        # four per SIMD would cut 28-step chunks: three per SIMD
+    ((8, 4096, 384, 16), 64),        # 52 -> 64
+    ((8, 1024, 512, 16), 24),        # 16 -> 24
+    ((2, 64, 32, 16), 8),            # the minimum chunk binds
+    ((256, 4096, 5120, 16), 4096),   # enough waves without cutting the sequence
+])
+def test_auto_plan(lib, shape, T):
+    b, L, D, N = shape
+    assert plan(lib, batch=b, L=L, D=D, N=N)[0] == T
+
+
 def test_plan_respects_chunk_len(lib):
     for cl in (1, 7, 64, 100, 5000):
         T, ws = plan(lib, batch=2, L=1000, D=64, N=16, chunk_len=cl)
