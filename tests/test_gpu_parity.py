@@ -96,6 +96,34 @@ def test_workload_conv():
     _full_compare("conv")
 
 
+# Medium shapes whose automatic plan takes the three-waves-per-SIMD branch
+# (four waves per SIMD would cut chunks shorter than 64 steps), compared in
+# full; the plan's chunk length is checked so the branch stays covered.
+# (batch, L, D, N, in, out, zoh, conv_k, planned chunk length)
+PLAN_SHAPES = [
+    (4, 2048, 768, 16, "f32", "f32", False, 0, 32),
+    (8, 4096, 384, 16, "bf16", "bf16", True, 4, 64),
+    (2, 2048, 1024, 16, "f32", "bf16", False, 0, 24),
+]
+
+
+@pytest.mark.parametrize("case", PLAN_SHAPES, ids=lambda c: "b%d_L%d_D%d_%s_zoh%d_k%d_T%d" % (
+    c[0], c[1], c[2], c[4], c[6], c[7], c[8]))
+def test_planned_medium_shapes(case):
+    Bt, L, D, N, idt, odt, zoh, K, T = case
+    shape = lambda *s: torch.empty(*s, dtype=G.torch_dtype(idt), device="cuda")
+    args = ssm.make_scan_args(shape(Bt, L, D), shape(Bt, L, D),
+                              torch.empty(D, N, device="cuda"), shape(Bt, L, N), shape(Bt, L, N))
+    assert ssm.plan_chunk_len(args) == T
+    w = SI.Workload("plan", 8, Bt, L, D, N, idt, odt, zoh=zoh, conv_k=K,
+                    delta_dist="loguniform", dskip_dist="uniform")
+    inp = SI.scan_inputs(w, seed=1100 + PLAN_SHAPES.index(case), h0=True)
+    G.say("case", case)
+    y, hl = G.gpu_scan(inp, idt, odt, zoh=zoh, h0=True)
+    y_ref, h_ref = G.oracle_scan(inp, zoh=zoh, h0=True)
+    G.say(G.compare(y, y_ref, G.y_tol(idt, odt), "y"), G.compare(hl, h_ref, G.TOL[idt], "h_last"))
+
+
 def _sampled_channels(inp, w, y, hl, chans):
     tol = G.TOL[w.in_dtype]
     for b, ds in chans:
