@@ -76,6 +76,7 @@ int64_t saved_count(int64_t L) {
 // 14.8 ms grouped vs 19.0 ms sequential).
 constexpr int64_t kGroupWalk = 64;
 constexpr int64_t kGroupChains = 65536;
+constexpr int64_t kBwdShortChunk = 128;   // backward super-chunk length, see make_bwd_plan
 
 struct Grouping {
   int64_t G = 0, gsz = 0;   // groups of gsz chunks (G = 0: one sequential walk)
@@ -475,6 +476,15 @@ BwdPlan make_bwd_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t super
     const int64_t waves = Bt * pl.dtiles;
     const int64_t cs = std::max<int64_t>(1, std::min<int64_t>(kTargetWaves / waves, pl.Cf));
     fines = (pl.Cf + cs - 1) / cs;
+    // Super-chunks longer than kBwdShortChunk steps are cut to that length
+    // when the reverse carry walk then still crosses at most kGroupWalk of
+    // them.  Measured (backward from kept states): 4 x 8192 x 2560 x 16 bf16
+    // ZOH, 336-step super-chunks 2.35-2.41 ms, 128-step 2.23 ms; 8 x 2048 x
+    // 1536 x 16 fp32 keeps its 112 steps (96-128 equal).  With many
+    // super-chunks the sequential walk grows long: 1 x 2^20 x 512 x 16 keeps
+    // 2048 steps (64-step super-chunks took 17.3 vs 10.0 ms).
+    if (fines * F > kBwdShortChunk && (L + kBwdShortChunk - 1) / kBwdShortChunk <= kGroupWalk)
+      fines = kBwdShortChunk / F;
   }
   // the reverse summary addresses a super-chunk's rows with 32-bit offsets
   const int64_t max_fines = std::max<int64_t>(1, kMaxChunkBytes / (D * 4) / F);

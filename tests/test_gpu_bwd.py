@@ -98,6 +98,14 @@ def test_bwd_planned_size(idt):
     G.say(reps)
 
 
+def test_bwd_planned_short_super_chunks():
+    """Many channels and a moderate length: the plan's super-chunks (160
+    steps here, from the wave target) are cut to 128 steps because the
+    reverse carry walk then still crosses only 16 of them."""
+    _, reps = run_case(2, 2048, 9216, 4, "bf16", True, True, True, True, 0, seed=3101)
+    G.say(reps)
+
+
 def test_bwd_deterministic():
     """Two calls give bitwise-identical gradients (partials are summed in a
     fixed order)."""
