@@ -18,15 +18,19 @@ measured per launch with HIP events that the library records around that
 kernel on the launch stream.  Two roofs are evaluated:
   hbm  algorithmic bytes of the call / duration vs 8000 GB/s;
   alu  algorithmic VALU lane-slots / duration vs 256 CU x 4 SIMD x 16 lanes
-       x 2.4 GHz = 39.3 T lane-slots/s, where an element costs 6 slots for
-       Delta*B (v_mul, v_exp at half rate = 2, v_mul, v_fma, v_fma) or 8 for
-       ZOH, plus 2 slots per (b, t, d) (Delta*u and the skip term).
+       x 2.4 GHz = 39.3 T lane-slots/s, where an element costs 5 issue slots
+       for Delta*B (v_mul, v_exp, v_mul, v_fma, v_fma) or 7 for ZOH, plus 2
+       slots per (b, t, d) (Delta*u and the skip term).  A transcendental
+       (v_exp, v_log, v_rcp) counts one issue slot: its unit works at half
+       rate, but beside other VALU work that second cycle overlaps (the long
+       scan's output pass retires 6.6e12 elements/s, more than 6 slots per
+       element would allow even at 2.4 GHz).
 The reported bound is the roof with the higher utilisation.
 
 --backward times ssm_scan_bwd instead: the gradients of the same workload's
 scan for upstream gradients dy ~ N(0, 1) and dh_last ~ N(0, 1); the roofline
 entry is that of the main backward kernel k_bwd_main (VALU lane-slots per
-element: 20 for Delta*B, 28 for ZOH -- the forward recompute plus the
+element: 18 for Delta*B, 26 for ZOH -- the forward recompute plus the
 adjoint step, its four gradient products and the channel-sum adds).  The
 backward starts from the states the forward scan kept every 16 steps
 (h_saved, written by one forward call before the timed region, as in
@@ -134,19 +138,19 @@ def decode_bytes(w, fused=False) -> int:
     return n
 
 
-# VALU lane-slots per (b, t, d) of the fused steps: softplus (bias add, scale,
-# exp (2), 1 + e, compare + select, log (2), 2 muls, sub, rcp (2)) and the
-# gate (scale, exp (2), add, rcp (2), 2 muls)
-SLOTS_BWD_ELEM = {False: 20.0, True: 28.0}   # k_bwd_main, keyed by ZOH
-SLOTS_SOFTPLUS = 15.0
-SLOTS_GATE = 8.0
+# VALU issue slots per (b, t, d) of the fused steps: softplus (bias add,
+# scale, exp, 1 + e, compare + select, log, 2 muls, sub, rcp) and the gate
+# (scale, exp, add, rcp, 2 muls); a transcendental counts one slot
+SLOTS_BWD_ELEM = {False: 18.0, True: 26.0}   # k_bwd_main, keyed by ZOH
+SLOTS_SOFTPLUS = 12.0
+SLOTS_GATE = 6.0
 
 
 def algorithmic_slots(w, fused=False) -> float:
-    per_elem = 8.0 if w.zoh else 6.0
+    per_elem = 7.0 if w.zoh else 5.0
     per_btd = 2.0
     if w.conv_k:
-        per_btd += 4 + 2 + 2 + 2   # 4 taps, exp (2), rcp (2), add + mul of SiLU
+        per_btd += 4 + 1 + 1 + 2   # 4 taps, exp, rcp, add + mul of SiLU
     if fused:
         per_btd += SLOTS_SOFTPLUS + SLOTS_GATE
     Bt, L, D, N = w.batch, w.seqlen, w.dim, w.dstate

@@ -40,9 +40,19 @@ ssm_status_t fail(ssm_status_t s, const char* fmt, ...) {
 // 384 x 16, 52 vs 64 steps, 93 vs 84 us.  At 64 steps and more, three and
 // four waves per SIMD measured the same or four better (the bench workloads
 // keep their plans).
+// Where the wave target already cuts the sequence into kBalanceChunks or
+// more chunks, chunks are also capped at kLongChunk steps.  The summary pass
+// then covers at least 15/16 of the elements anyway, so more chunks add
+// little work, while many shorter waves let the dispatcher even out the
+// SIMDs: 4096 waves of thousands of steps each cannot.  Measured on
+// 1 x 2^20 x 512 x 16 bf16 (whole scan): 2048-step chunks 2.87 ms, 1024
+// 2.61, 512 2.52, 256 2.50, 128 2.60; 4 x 8192 x 2560 x 16 bf16 with ZOH and
+// the conv: 328 steps 677 us, 256 steps 661 us.
 constexpr int64_t kTargetWaves = 4096;
 constexpr int64_t kShortTargetWaves = 3072;
 constexpr int64_t kShortChunk = 64;
+constexpr int64_t kBalanceChunks = 16;
+constexpr int64_t kLongChunk = 256;
 constexpr int64_t kMinChunk = 8;
 constexpr int64_t kChunkAlign = 4;
 constexpr int64_t kMaxChunk = int64_t(1) << 30;   // kernels count steps in 32 bits
@@ -122,6 +132,7 @@ Plan make_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t chunk_len) {
     if (C > 1 && (L + C - 1) / C < kShortChunk) C = chunks(kShortTargetWaves);
     T = (L + C - 1) / C;
     if (C > 1) T = (T + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+    if (C >= kBalanceChunks) T = std::min(T, kLongChunk);
     T = std::min(T, L);
   }
   pl.T = std::min({T, kMaxChunk, std::max<int64_t>(1, kMaxChunkBytes / (D * 4))});

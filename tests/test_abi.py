@@ -443,8 +443,9 @@ def test_plan_and_workspace(lib, shape):
 
 @pytest.mark.parametrize("shape,T", [
     ((8, 2048, 1536, 16), 100),      # 192 wave columns x 21 chunks = 4032 waves
-    ((4, 8192, 2560, 16), 328),      # 160 x 25 = 4000
-    ((1, 1 << 20, 512, 16), 2048),   # 8 x 512 = 4096
+    ((4, 8192, 2560, 16), 256),      # 25 chunks of 328 at the wave target: capped at 256 steps
+    ((1, 1 << 20, 512, 16), 256),    # 512 chunks of 2048: capped at 256 steps
+    ((16, 2048, 2560, 16), 344),     # 6 chunks: too few for the cap
     ((1, 16384, 1024, 16), 64),      # 64-step chunks at four waves per SIMD stay
     ((4, 2048, 768, 16), 32),        # four per SIMD would cut 28-step chunks: three per SIMD
     ((8, 4096, 384, 16), 64),        # 52 -> 64

@@ -55,12 +55,15 @@ def test_state_and_fused_extras():
 
 
 def test_scan_slots():
-    """VALU lane-slots: 6 per element for Delta*B (exp counts 2; mul, mul,
-    fma, fma), 8 for ZOH, plus 2 per (b, t, d) (Delta*u and the skip term)."""
+    """VALU issue slots: 5 per element for Delta*B (mul, exp, mul, fma, fma;
+    a transcendental issues in one slot), 7 for ZOH, plus 2 per (b, t, d)
+    (Delta*u and the skip term); the conv prologue adds 8 per (b, t, d)."""
     w = SI.WORKLOADS["fp32"]
-    assert bench.algorithmic_slots(w) == pytest.approx(w.elems * 6 + 8 * 2048 * 1536 * 2)
+    assert bench.algorithmic_slots(w) == pytest.approx(w.elems * 5 + 8 * 2048 * 1536 * 2)
     long_ = SI.WORKLOADS["long"]
-    assert bench.algorithmic_slots(long_) == pytest.approx(long_.elems * 6 + (1 << 20) * 512 * 2)
+    assert bench.algorithmic_slots(long_) == pytest.approx(long_.elems * 5 + (1 << 20) * 512 * 2)
+    conv = SI.WORKLOADS["conv"]
+    assert bench.algorithmic_slots(conv) == pytest.approx(conv.elems * 7 + 4 * 8192 * 2560 * 10)
 
 
 def test_decode_bytes():
