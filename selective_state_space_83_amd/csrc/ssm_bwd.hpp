@@ -66,6 +66,9 @@ struct BwdParams {
   float* dDp;            // (Bt * Cs, D)
   float* dBp;            // (Bt, L, dtiles, N) per-tile dB partials
   float* dCp;            // (Bt, L, dtiles, N)
+  float* rgS;            // (Bt, rG, D) grouped reverse walk: sums of Delta per group
+  float* rgB;            // (Bt, rG, D, N) adjoint of a group from zero, then its carry in
+  int64_t rG, rgsz;      // groups of rgsz super-chunks (rG = 0: one sequential walk)
   int64_t Bt, L, D;
   int64_t Ts;            // super-chunk length (a multiple of kBwdFine)
   int64_t Cs, Cf;        // super-chunks, fine chunks
@@ -327,6 +330,66 @@ __global__ void __launch_bounds__(kWave) k_bwd_combine(const BwdParams p) {
     carry = fmaf(expm1_from(z2, exp2_fast(z2)), carry, carry + p.gsum[slot * DN + dn]);
     p.gsum[slot * DN + dn] = carry;
   }
+}
+
+// The same walk in groups, for few chains over many super-chunks: the
+// super-chunks are taken from the last to the first (reversed index r is slot
+// Cs - 2 - r), so the forward's walk helpers apply with negative strides.
+// Group g of rgsz consecutive reversed super-chunks is folded from zero
+// (k_bwd_rgroups), the groups are walked from dh_last (k_bwd_rtop), and each
+// group is walked again from its carry, writing the carries (k_bwd_rapply).
+template <int N>
+__device__ __forceinline__ void rev_walk_ptrs(const BwdParams& p, int64_t b, int64_t d, int64_t dn,
+                                              const float** ds, float** hs) {
+  const int64_t nc = p.Cs - 1;
+  *ds = p.dsum_s + (b * nc + nc - 1) * p.D + d;
+  *hs = p.gsum + (b * nc + nc - 1) * p.D * N + dn;
+}
+
+template <int N>
+__global__ void __launch_bounds__(kWave) k_bwd_rgroups(const BwdParams p) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kWave + threadIdx.x;
+  const int64_t DN = p.D * N;
+  if (idx >= p.Bt * p.rG * DN) return;
+  const int64_t bg = idx / DN, dn = idx - bg * DN;
+  const int64_t b = bg / p.rG, g = bg - b * p.rG;
+  const int64_t d = dn / N;
+  const int64_t nc = p.Cs - 1;
+  const int64_t c0 = g * p.rgsz, c1 = (c0 + p.rgsz < nc) ? c0 + p.rgsz : nc;
+  const float* ds;
+  float* hs;
+  rev_walk_ptrs<N>(p, b, d, dn, &ds, &hs);
+  float ssum = 0.0f;
+  p.rgB[idx] = walk_chunks<false, true>(p.A[dn] * kLog2e, 0.0f, ds, -p.D, hs, -DN, c0, c1, &ssum);
+  if (dn % N == 0) p.rgS[bg * p.D + d] = ssum;
+}
+
+template <int N>
+__global__ void __launch_bounds__(kWave) k_bwd_rtop(const BwdParams p) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kWave + threadIdx.x;
+  const int64_t DN = p.D * N;
+  if (idx >= p.Bt * DN) return;
+  const int64_t b = idx / DN, dn = idx - b * DN;
+  const int64_t d = dn / N;
+  const float carry = p.dh_last ? p.dh_last[idx] : 0.0f;
+  walk_carry_in(p.A[dn] * kLog2e, carry, p.rgS + b * p.rG * p.D + d, p.D,
+                p.rgB + b * p.rG * DN + dn, DN, p.rG);
+}
+
+template <int N>
+__global__ void __launch_bounds__(kWave) k_bwd_rapply(const BwdParams p) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kWave + threadIdx.x;
+  const int64_t DN = p.D * N;
+  if (idx >= p.Bt * p.rG * DN) return;
+  const int64_t bg = idx / DN, dn = idx - bg * DN;
+  const int64_t b = bg / p.rG, g = bg - b * p.rG;
+  const int64_t d = dn / N;
+  const int64_t nc = p.Cs - 1;
+  const int64_t c0 = g * p.rgsz, c1 = (c0 + p.rgsz < nc) ? c0 + p.rgsz : nc;
+  const float* ds;
+  float* hs;
+  rev_walk_ptrs<N>(p, b, d, dn, &ds, &hs);
+  walk_chunks<true, false>(p.A[dn] * kLog2e, p.rgB[idx], ds, -p.D, hs, -DN, c0, c1, nullptr);
 }
 
 // ---------------------------------------------------------------------------

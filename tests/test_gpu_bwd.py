@@ -106,6 +106,25 @@ def test_bwd_planned_short_super_chunks():
     G.say(reps)
 
 
+# (batch, L, D, N, in dtype, zoh, super-chunk): the reverse carry walk over
+# more than 64 super-chunks with fewer than 65536 chains runs in groups
+GROUPED_WALK = [
+    (1, 4096, 64, 16, "f32", False, 16),    # 255 carries: 16 groups of 16
+    (2, 2048, 130, 16, "bf16", True, 16),   # 127 carries: 12 groups, the last of 6
+    (1, 2100, 33, 4, "f32", False, 32),     # 65 carries: 9 groups, the last of 1
+    (1, 2048, 33, 4, "f32", True, 32),      # 63 carries: one sequential walk
+]
+
+
+@pytest.mark.parametrize("case", GROUPED_WALK, ids=lambda c: "b%d_L%d_D%d_N%d_%s_zoh%d_sc%d" % c)
+def test_bwd_grouped_reverse_walk(case):
+    Bt, L, D, N, idt, zoh, sc = case
+    G.say("case", case)
+    _, reps = run_case(Bt, L, D, N, idt, zoh, True, True, True, sc,
+                       seed=3300 + GROUPED_WALK.index(case))
+    G.say(reps)
+
+
 def test_bwd_deterministic():
     """Two calls give bitwise-identical gradients (partials are summed in a
     fixed order)."""
