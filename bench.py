@@ -1,17 +1,23 @@
 #!/usr/bin/env python3
 """Throughput of the selective-scan forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fp32]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
 
 A step is one ssm_scan_fwd call over the whole workload (every pass of the
 hot path: chunk summaries, carry combine, output pass) on inputs already
 resident in HBM.  W untimed steps, then exactly K timed steps between two
-device synchronizations.  Prints one JSON line.
+device synchronizations, each step right after a 1 GiB write that evicts L2
+and the Infinity Cache (so every step streams its inputs from HBM); the
+headline (value, ms_per_step, hbm_gbps) is the median of those K flushed
+steps.  K more steps run back to back afterwards and are reported as the
+warm figures (warm_ms_per_step, ...).  Prints one JSON line.
 
-The default workload is the fp32 scan batch=8, L=2048, D=1536, N=16 (x, B,
-C ~ N(0,1), Delta log-uniform in [1e-3, 0.1], A_log[d,n] = log(n+1),
-D_skip ~ U(0.5, 1.5)).  The decode workload times 512 consecutive ssm_step
-calls as one step.
+The default workload is the largest scan: batch=1, L=1,048,576, D=512, N=16,
+bf16 x, Delta, B, C and y with fp32 state (x, B, C ~ N(0,1), Delta =
+softplus(0.5 N(0,1) - 4), A_log[d,n] = log(n+1), D_skip = 1).  The others:
+tiny, fp32 (8 x 2048 x 1536 x 16 fp32), conv (4 x 8192 x 2560 x 16 bf16 with
+the conv prologue and exact ZOH) and decode (512 consecutive ssm_step calls
+on 256 x 5120 x 16 timed as one step).
 
 Roofline of the dominant kernel (the output pass k_scan_out): its duration is
 measured per launch with HIP events that the library records around that
@@ -237,43 +243,47 @@ def bench_scan(w, steps, warmup, torch, ssm, chunk_len=0, fused=False):
     ws_bytes = ssm.workspace_size(prep.args)
     chunk = ssm.plan_chunk_len(prep.args)
     hip = HipEvents()
-    evs = hip.create(2 * steps)
+    evs = hip.create(4 * steps)       # the output pass of every timed step, both loops
     stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
 
     def call(i=None):
         ev = (evs[2 * i], evs[2 * i + 1]) if i is not None else None
         prep.run(stream=stream, events=ev)
 
+    def ev_pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
+    # timed region: K steps, each right after a cache-evicting write (the
+    # write is outside each step's event pair)
     t0 = time.perf_counter()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
+    pairs = [ev_pair() for _ in range(steps)]
     for i in range(steps):
+        flush.fill_(1)
+        pairs[i][0].record(stream)
         call(i)
-    e1.record(stream)
+        pairs[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = e0.elapsed_time(e1)
+    flushed_ms = [a.elapsed_time(b) for a, b in pairs]
     out_ms = [hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)]
+    # warm: K more steps back to back
+    e0, e1 = ev_pair()
+    e0.record(stream)
+    for i in range(steps):
+        call(steps + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm_total_ms = e0.elapsed_time(e1)
+    out_ms_warm = [hip.elapsed_ms(evs[2 * (steps + i)], evs[2 * (steps + i) + 1])
+                   for i in range(steps)]
     hip.destroy(evs)
-
-    # the same call with L2/MALL flushed before each one (events around the call only)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    fl = []
-    for _ in range(min(steps, 20)):
-        flush.fill_(1)
-        a0 = torch.cuda.Event(enable_timing=True)
-        a1 = torch.cuda.Event(enable_timing=True)
-        a0.record(stream)
-        call()
-        a1.record(stream)
-        torch.cuda.synchronize()
-        fl.append(a0.elapsed_time(a1))
     del flush
-    return dict(inp=inp, total_ms=total_ms, wall_s=wall, out_ms=out_ms, flushed_ms=fl,
+    return dict(inp=inp, flushed_ms=flushed_ms, wall_s=wall, out_ms=out_ms,
+                warm_ms=warm_total_ms / steps, out_ms_warm=out_ms_warm,
                 chunk_len=chunk, chunks=-(-w.seqlen // chunk), workspace=ws_bytes)
 
 
@@ -381,42 +391,62 @@ def bench_bwd(w, steps, warmup, torch, ssm, kept=True, train=False):
 
 
 def cpu_baseline(w, inp, budget_s=20.0, min_s=10.0):
-    """The oracle, untuned, on this host's cores: whole batch rows of the same
-    workload, as many as fit the CPU budget (at least one); when the whole
-    workload takes less than min_s, whole passes over it are repeated until
-    min_s has elapsed, so the rate is timed over seconds of work."""
+    """The oracle, untuned, on this host's cores, over a bounded sample of the
+    same workload: whole batch rows when a row takes at most half the budget
+    (whole passes over the batch repeated until min_s has elapsed when the
+    whole workload is quicker than that), otherwise consecutive 64-channel
+    blocks of the batch rows (wrapping around) until min_s has elapsed."""
     import oracle
     cores = len(os.sched_getaffinity(0))
     orc = oracle.default()
 
-    def run(lo, hi):
+    def run(r0, r1, d0=0, d1=None):
+        d1 = w.dim if d1 is None else d1
+        sl = lambda a: a[r0:r1, :, d0:d1]
+        ch = lambda a: None if a is None else a[d0:d1]
         t = time.perf_counter()
-        orc.scan(inp["x"][lo:hi], inp["delta"][lo:hi], inp["A"], inp["B"][lo:hi],
-                 inp["C"][lo:hi], inp["D"], conv_w=inp.get("conv_w"), conv_b=inp.get("conv_b"),
-                 zoh=w.zoh, want_h_last=False, nthreads=cores)
+        orc.scan(sl(inp["x"]), sl(inp["delta"]), ch(inp["A"]), inp["B"][r0:r1],
+                 inp["C"][r0:r1], ch(inp["D"]), conv_w=ch(inp.get("conv_w")),
+                 conv_b=ch(inp.get("conv_b")), zoh=w.zoh, want_h_last=False, nthreads=cores)
         return time.perf_counter() - t
 
-    # time one batch row first, then scale the sample to the budget
-    dt = run(0, 1)
-    rows = 1
-    extra = int(min(w.batch - 1, max(0, budget_s / max(dt, 1e-6) - 1)))
-    if extra > 0:
-        dt += run(1, 1 + extra)
-        rows += extra
-    passes = 1
-    if rows == w.batch:
-        while dt < min_s:
-            dt += run(0, w.batch)
-            passes += 1
-    elems = w.seqlen * w.dim * w.dstate
-    if passes > 1:
-        what = "%d passes over all %d batch rows" % (passes, w.batch)
+    blk = min(64, w.dim)
+    dt = run(0, 1, 0, blk)          # probe: one block of row 0
+    per_row = dt * w.dim / blk
+    if per_row <= budget_s / 2:
+        dt = run(0, 1)
+        rows = 1
+        extra = int(min(w.batch - 1, max(0, budget_s / max(dt, 1e-6) - 1)))
+        if extra > 0:
+            dt += run(1, 1 + extra)
+            rows += extra
+        passes = 1
+        if rows == w.batch:
+            while dt < min_s:
+                dt += run(0, w.batch)
+                passes += 1
+        elems = (rows + (passes - 1) * w.batch) * w.seqlen * w.dim * w.dstate
+        if passes > 1:
+            what = "%d passes over the whole workload (%d batch row%s" % (
+                passes, w.batch, "s" if w.batch > 1 else "")
+        else:
+            what = "%d of %d batch rows (" % (rows, w.batch)
+        sample = "%s of %d x %d x %d elems)" % (what, w.seqlen, w.dim, w.dstate)
     else:
-        what = "%d of %d batch rows" % (rows, w.batch)
-    return {"value": (rows + (passes - 1) * w.batch) * elems / dt, "unit": "elem/s",
-            "cores": cores, "kind": "oracle",
-            "sample": "%s (%d x %d x %d elems each), fp64 sequential recurrence, %.1f s wall"
-                      % (what, w.seqlen, w.dim, w.dstate, dt),
+        nblk = 1
+        k = 1
+        nb = -(-w.dim // blk)
+        while dt < min_s:
+            r, j = divmod(k, nb)
+            d0 = j * blk
+            dt += run(r % w.batch, r % w.batch + 1, d0, min(w.dim, d0 + blk))
+            nblk += 1
+            k += 1
+        elems = nblk * w.seqlen * blk * w.dstate
+        sample = ("%d consecutive blocks of %d channels of a batch row (1 x %d x %d x %d "
+                  "elems each)" % (nblk, blk, w.seqlen, blk, w.dstate))
+    return {"value": elems / dt, "unit": "elem/s", "cores": cores, "kind": "oracle",
+            "sample": "%s, fp64 sequential recurrence, %.1f s wall" % (sample, dt),
             "single_thread": cpu_single_thread(w, inp, orc)}
 
 
@@ -510,7 +540,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="fp32")
+    ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward scan (ssm_scan_bwd) of the workload")
@@ -608,9 +638,10 @@ def main():
         return
 
     r = bench_scan(w, args.steps, args.warmup, torch, ssm, args.chunk_len, fused=args.fused)
-    ms = r["total_ms"] / args.steps
+    ms = float(np.median(r["flushed_ms"]))
     elems = w.elems
     out_us = float(np.mean(r["out_ms"])) * 1e3
+    out_us_warm = float(np.mean(r["out_ms_warm"])) * 1e3
     abytes = algorithmic_bytes(w, fused=args.fused)
     slots = algorithmic_slots(w, fused=args.fused)
     hbm_ach = abytes / (out_us * 1e-6) / 1e9
@@ -626,6 +657,7 @@ def main():
                 "frac": hbm_frac, "traffic": traffic}
     roof["kernel"] = "k_scan_out"
     roof["kernel_us"] = out_us
+    roof["kernel_us_warm"] = out_us_warm
     copy = copy_bandwidth(torch)
     roof["hbm_view"] = {"achieved_gbps": hbm_ach, "frac": hbm_frac, "copy_gbps": copy,
                         "frac_of_copy": hbm_ach / copy}
@@ -644,10 +676,12 @@ def main():
                       "dstate": w.dstate, "in_dtype": w.in_dtype, "out_dtype": w.out_dtype,
                       "disc": "zoh" if w.zoh else "delta_b", "conv_k": w.conv_k,
                       "chunk_len": r["chunk_len"], "chunks": r["chunks"],
+                      "timing": "median of K steps, each after a 1 GiB cache-evicting write",
                       "fused": ("softplus+gate" + ("+conv_state" if w.conv_k else ""))
                       if args.fused else None},
            "hbm_gbps": whole_gbps, "hbm_frac": whole_gbps / HBM_PEAK_GBS,
-           "flushed_ms_per_step": float(np.median(r["flushed_ms"])),
+           "warm_ms_per_step": r["warm_ms"], "warm_value": elems / (r["warm_ms"] * 1e-3),
+           "warm_hbm_gbps": abytes / (r["warm_ms"] * 1e-3) / 1e9,
            "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
 

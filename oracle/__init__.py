@@ -34,6 +34,8 @@ def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
 class Oracle:
     """ctypes view of one build of the oracle library."""
 
+    GRADS = ("dx", "ddelta", "dA", "dB", "dC", "dD", "dh0")   # order of the C arguments
+
     def __init__(self, path: str = _LIB_PATH):
         if not os.path.exists(path):
             build(out=path)
@@ -50,6 +52,9 @@ class Oracle:
         lib.ssm_ref_scan_bwd_f64.argtypes = [i64, i64, i64, i64, dp, dp, dp, dp, dp, dp, dp,
                                              dp, dp, ci, dp, dp, dp, dp, dp, dp, dp, ci]
         lib.ssm_ref_scan_bwd_f64.restype = ctypes.c_int
+        lib.ssm_ref_scan_bwd_mag_f64.argtypes = ([i64, i64, i64, i64] + [dp] * 9 + [ci]
+                                                 + [dp] * 14 + [ci])
+        lib.ssm_ref_scan_bwd_mag_f64.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -142,11 +147,17 @@ class Oracle:
         return (y, h) if conv_w is None else (y, h, cs)
 
     def scan_bwd(self, x, delta, A, B, C, dy, D=None, h0=None, dh_last=None, zoh=False,
-                 nthreads=0):
+                 nthreads=0, mag=False):
         """Gradients of sum(dy * y) + sum(dh_last * h_last) for the scan
         without conv prologue.  Returns a dict of float64 arrays: dx, ddelta
         (batch, L, dim), dA (dim, N), dB, dC (batch, L, N), dD (dim,), dh0
-        (batch, dim, N)."""
+        (batch, dim, N).
+
+        With ``mag=True`` returns (gradients, magnitudes): the second dict has
+        the same keys and shapes and holds, for every entry, its chain-rule
+        sum with every term and every quantity inside a term replaced by its
+        absolute value -- the scale against which the rounding error of that
+        one entry is bounded, in any evaluation order."""
         x, delta, A, B, C, dy = map(self._f64, (x, delta, A, B, C, dy))
         D, h0, dh_last = map(self._f64, (D, h0, dh_last))
         batch, L, dim = x.shape
@@ -159,17 +170,18 @@ class Oracle:
         g = {"dx": np.zeros(x.shape), "ddelta": np.zeros(x.shape), "dA": np.zeros((dim, N)),
              "dB": np.zeros(B.shape), "dC": np.zeros(C.shape), "dD": np.zeros(dim),
              "dh0": np.zeros((batch, dim, N))}
-        rc = self.lib.ssm_ref_scan_bwd_f64(batch, L, dim, N, self._ptr(x), self._ptr(delta),
-                                           self._ptr(A), self._ptr(B), self._ptr(C),
-                                           self._ptr(D), self._ptr(h0), self._ptr(dy),
-                                           self._ptr(dh_last), int(bool(zoh)),
-                                           self._ptr(g["dx"]), self._ptr(g["ddelta"]),
-                                           self._ptr(g["dA"]), self._ptr(g["dB"]),
-                                           self._ptr(g["dC"]), self._ptr(g["dD"]),
-                                           self._ptr(g["dh0"]), int(nthreads))
+        common = [batch, L, dim, N, self._ptr(x), self._ptr(delta), self._ptr(A), self._ptr(B),
+                  self._ptr(C), self._ptr(D), self._ptr(h0), self._ptr(dy), self._ptr(dh_last),
+                  int(bool(zoh))] + [self._ptr(g[k]) for k in self.GRADS]
+        if not mag:
+            rc = self.lib.ssm_ref_scan_bwd_f64(*common, int(nthreads))
+        else:
+            m = {k: np.zeros_like(v) for k, v in g.items()}
+            rc = self.lib.ssm_ref_scan_bwd_mag_f64(*common, *[self._ptr(m[k]) for k in self.GRADS],
+                                                   int(nthreads))
         if rc != 0:
             raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
-        return g
+        return (g, m) if mag else g
 
 
 _default = None

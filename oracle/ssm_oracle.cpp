@@ -181,6 +181,15 @@ struct BwdProblem {
   const double *x, *delta, *A, *Bm, *Cm, *Dskip, *h0, *dy, *dh_last;
   int zoh;
   double *dx, *ddelta, *dB, *dC, *dh0;   // dB, dC: rows of the batch rows a worker owns
+  // Optional magnitudes (all NULL, or all given with the gradients' shapes):
+  // for every gradient entry, the same chain-rule sum with every term, and
+  // every quantity inside a term (states, adjoints, inputs), replaced by its
+  // absolute value.  A sum evaluated in any order and precision with unit
+  // roundoff u then differs from the exact one by at most about
+  // (depth * u) times this magnitude (running error analysis), so a test can
+  // bound each entry's error by a multiple of its own magnitude instead of
+  // the largest entry of the tensor.
+  double *mx, *mdelta, *mB, *mC, *mh0;
 };
 
 // d(input factor)/d(Delta) and d(input factor)/dA for the factor f used in
@@ -206,30 +215,40 @@ void factor_derivs(double dt, double a_cont, int zoh, double* df_dt, double* df_
 // Gradients for batch row b (all channels), accumulating dA (D, N) and
 // dD (D) into the worker's own buffers.
 void bwd_batch_row(const BwdProblem& p, int64_t b, std::vector<double>& dA,
-                   std::vector<double>& dD) {
+                   std::vector<double>& dD, std::vector<double>& mA, std::vector<double>& mD) {
   const int64_t L = p.seqlen, D = p.dim, N = p.dstate;
+  const bool mag = p.mx != nullptr;
   std::vector<double> H((L + 1) * N);   // H[(t + 1) * N + n] = h_t[n], row 0 = h_{-1}
   std::vector<double> g(N);
+  // magnitudes of the states and adjoints (used only when `mag`)
+  std::vector<double> Hm(mag ? (L + 1) * N : 0), gm(mag ? N : 0);
   for (int64_t d = 0; d < D; ++d) {
     // forward sweep keeping every state
     for (int64_t n = 0; n < N; ++n) H[n] = p.h0 ? p.h0[(b * D + d) * N + n] : 0.0;
+    if (mag)
+      for (int64_t n = 0; n < N; ++n) Hm[n] = std::fabs(H[n]);
     for (int64_t t = 0; t < L; ++t) {
       const double u = p.x[(b * L + t) * D + d];
       const double dt = p.delta[(b * L + t) * D + d];
       for (int64_t n = 0; n < N; ++n) {
         const double a_cont = p.A[d * N + n];
-        H[(t + 1) * N + n] = std::exp(dt * a_cont) * H[t * N + n] +
-                             input_factor(dt, a_cont, p.zoh) * p.Bm[(b * L + t) * N + n] * u;
+        const double abar = std::exp(dt * a_cont);
+        const double inp = input_factor(dt, a_cont, p.zoh) * p.Bm[(b * L + t) * N + n] * u;
+        H[(t + 1) * N + n] = abar * H[t * N + n] + inp;
+        if (mag) Hm[(t + 1) * N + n] = abar * Hm[t * N + n] + std::fabs(inp);
       }
     }
     // reverse sweep: g[n] is dLoss/dh_t[n] once token t's output term is added
     for (int64_t n = 0; n < N; ++n) g[n] = p.dh_last ? p.dh_last[(b * D + d) * N + n] : 0.0;
+    if (mag)
+      for (int64_t n = 0; n < N; ++n) gm[n] = std::fabs(g[n]);
     const double dskip = p.Dskip ? p.Dskip[d] : 0.0;
     for (int64_t t = L - 1; t >= 0; --t) {
       const double u = p.x[(b * L + t) * D + d];
       const double dt = p.delta[(b * L + t) * D + d];
       const double gy = p.dy[(b * L + t) * D + d];
       double du = dskip * gy, ddt = 0.0;
+      double mdu = std::fabs(dskip * gy), mddt = 0.0;
       for (int64_t n = 0; n < N; ++n) {
         const double a_cont = p.A[d * N + n];
         const double Bn = p.Bm[(b * L + t) * N + n];
@@ -248,13 +267,30 @@ void bwd_batch_row(const BwdProblem& p, int64_t b, std::vector<double>& dA,
         ddt += G * (a_cont * abar * h_prev + df_dt * Bn * u);
         dA[d * N + n] += G * (dt * abar * h_prev + df_da * Bn * u);
         g[n] = abar * G;                                  // into h_{t-1}
+        if (mag) {
+          const double Gm = gm[n] + std::fabs(Cn * gy);
+          const double hpm = Hm[t * N + n], hnm = Hm[(t + 1) * N + n];
+          p.mC[(b * L + t) * N + n] += std::fabs(gy) * hnm;
+          p.mB[(b * L + t) * N + n] += Gm * std::fabs(f * u);
+          mdu += Gm * std::fabs(f * Bn);
+          mddt += Gm * (std::fabs(a_cont) * abar * hpm + std::fabs(df_dt * Bn * u));
+          mA[d * N + n] += Gm * (std::fabs(dt) * abar * hpm + std::fabs(df_da * Bn * u));
+          gm[n] = abar * Gm;
+        }
       }
       p.dx[(b * L + t) * D + d] = du;
       p.ddelta[(b * L + t) * D + d] = ddt;
       dD[d] += gy * u;
+      if (mag) {
+        p.mx[(b * L + t) * D + d] = mdu;
+        p.mdelta[(b * L + t) * D + d] = mddt;
+        mD[d] += std::fabs(gy * u);
+      }
     }
     if (p.dh0)
       for (int64_t n = 0; n < N; ++n) p.dh0[(b * D + d) * N + n] = g[n];
+    if (mag)
+      for (int64_t n = 0; n < N; ++n) p.mh0[(b * D + d) * N + n] = gm[n];
   }
 }
 
@@ -332,28 +368,56 @@ int ssm_ref_scan_bwd_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
                          const double* Bm, const double* Cm, const double* Dskip,
                          const double* h0, const double* dy, const double* dh_last, int zoh,
                          double* dx, double* ddelta, double* dA, double* dB, double* dC,
-                         double* dD, double* dh0, int nthreads) {
+                         double* dD, double* dh0, int nthreads);
+
+// O3 together with the magnitude of every gradient entry (see BwdProblem):
+// mx, mdelta (batch, L, D), mA (D, N), mB, mC (batch, L, N), mD (D) and mh0
+// (batch, D, N), all required.  The gradients are the same as
+// ssm_ref_scan_bwd_f64's (dD and dh0 required here too).
+int ssm_ref_scan_bwd_mag_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                             const double* x, const double* delta, const double* A,
+                             const double* Bm, const double* Cm, const double* Dskip,
+                             const double* h0, const double* dy, const double* dh_last,
+                             int zoh, double* dx, double* ddelta, double* dA, double* dB,
+                             double* dC, double* dD, double* dh0, double* mx, double* mdelta,
+                             double* mA, double* mB, double* mC, double* mD, double* mh0,
+                             int nthreads);
+
+}  // extern "C"
+
+namespace {
+
+int scan_bwd_impl(const BwdProblem& p0, double* dA, double* dD, double* mA, double* mD,
+                  int nthreads) {
+  const int64_t batch = p0.batch, seqlen = p0.seqlen, dim = p0.dim, dstate = p0.dstate;
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1) return -1;
-  if (!A || !dA) return -1;
-  if (batch * seqlen * dim > 0 && (!x || !delta || !Bm || !Cm || !dy || !dx || !ddelta ||
-                                   !dB || !dC))
+  if (!p0.A || !dA) return -1;
+  if (batch * seqlen * dim > 0 && (!p0.x || !p0.delta || !p0.Bm || !p0.Cm || !p0.dy ||
+                                   !p0.dx || !p0.ddelta || !p0.dB || !p0.dC))
     return -1;
+  const bool mag = p0.mx != nullptr;
   const int64_t D = dim, N = dstate;
   for (int64_t i = 0; i < D * N; ++i) dA[i] = 0.0;
   if (dD)
     for (int64_t i = 0; i < D; ++i) dD[i] = 0.0;
   if (batch * seqlen > 0) {
-    for (int64_t i = 0; i < batch * seqlen * N; ++i) dB[i] = dC[i] = 0.0;
+    for (int64_t i = 0; i < batch * seqlen * N; ++i) p0.dB[i] = p0.dC[i] = 0.0;
+  }
+  if (mag) {
+    for (int64_t i = 0; i < D * N; ++i) mA[i] = 0.0;
+    for (int64_t i = 0; i < D; ++i) mD[i] = 0.0;
+    for (int64_t i = 0; i < batch * seqlen * N; ++i) p0.mB[i] = p0.mC[i] = 0.0;
   }
   if (batch * dim == 0) return 0;
-  BwdProblem p{batch, seqlen, dim, dstate, x, delta, A, Bm, Cm, Dskip, h0, dy, dh_last, zoh,
-               dx, ddelta, dB, dC, dh0};
+  const BwdProblem& p = p0;
   const int nt = pick_threads(nthreads, batch);
   std::vector<std::vector<double>> dA_w(nt, std::vector<double>(D * N, 0.0));
   std::vector<std::vector<double>> dD_w(nt, std::vector<double>(D, 0.0));
+  std::vector<std::vector<double>> mA_w(nt, std::vector<double>(mag ? D * N : 0, 0.0));
+  std::vector<std::vector<double>> mD_w(nt, std::vector<double>(mag ? D : 0, 0.0));
   auto work = [&](int w) {
     for (int64_t b = batch * w / nt; b < batch * (w + 1) / nt; ++b)
-      bwd_batch_row(p, b, dA_w[w], dD_w[w]);
+      bwd_batch_row(p, b, dA_w[w], dD_w[w], mA_w[w], mD_w[w]);
   };
   std::vector<std::thread> pool;
   for (int w = 1; w < nt; ++w) pool.emplace_back(work, w);
@@ -363,8 +427,42 @@ int ssm_ref_scan_bwd_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
     for (int64_t i = 0; i < D * N; ++i) dA[i] += dA_w[w][i];
     if (dD)
       for (int64_t i = 0; i < D; ++i) dD[i] += dD_w[w][i];
+    if (mag) {
+      for (int64_t i = 0; i < D * N; ++i) mA[i] += mA_w[w][i];
+      for (int64_t i = 0; i < D; ++i) mD[i] += mD_w[w][i];
+    }
   }
   return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_ref_scan_bwd_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                         const double* x, const double* delta, const double* A,
+                         const double* Bm, const double* Cm, const double* Dskip,
+                         const double* h0, const double* dy, const double* dh_last, int zoh,
+                         double* dx, double* ddelta, double* dA, double* dB, double* dC,
+                         double* dD, double* dh0, int nthreads) {
+  const BwdProblem p{batch, seqlen, dim, dstate, x, delta, A, Bm, Cm, Dskip, h0, dy, dh_last,
+                     zoh, dx, ddelta, dB, dC, dh0, nullptr, nullptr, nullptr, nullptr,
+                     nullptr};
+  return scan_bwd_impl(p, dA, dD, nullptr, nullptr, nthreads);
+}
+
+int ssm_ref_scan_bwd_mag_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                             const double* x, const double* delta, const double* A,
+                             const double* Bm, const double* Cm, const double* Dskip,
+                             const double* h0, const double* dy, const double* dh_last,
+                             int zoh, double* dx, double* ddelta, double* dA, double* dB,
+                             double* dC, double* dD, double* dh0, double* mx, double* mdelta,
+                             double* mA, double* mB, double* mC, double* mD, double* mh0,
+                             int nthreads) {
+  if (!dD || !dh0 || !mx || !mdelta || !mA || !mB || !mC || !mD || !mh0) return -1;
+  const BwdProblem p{batch, seqlen, dim, dstate, x, delta, A, Bm, Cm, Dskip, h0, dy, dh_last,
+                     zoh, dx, ddelta, dB, dC, dh0, mx, mdelta, mB, mC, mh0};
+  return scan_bwd_impl(p, dA, dD, mA, mD, nthreads);
 }
 
 }  // extern "C"

@@ -22,6 +22,7 @@ no CPU fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Tuple
@@ -215,6 +216,17 @@ def _stream_handle(stream) -> Optional[int]:
     return s.cuda_stream
 
 
+def _on_stream(stream):
+    """Context in which the outputs and the workspace of a call are
+    allocated: the stream the call's kernels run on.  PyTorch's caching
+    allocator hands a freed block only to later allocations on the stream
+    it was allocated on, so a workspace freed when the call returns cannot
+    be given to other work while the call's kernels still use it."""
+    if stream is None:
+        return contextlib.nullcontext()
+    return _torch().cuda.stream(stream)
+
+
 def saved_states_shape(batch: int, seqlen: int, dim: int, dstate: int) -> tuple:
     """Shape of the states a scan keeps for the backward pass (h_saved): the
     state entering steps 16, 32, ... below seqlen."""
@@ -322,23 +334,25 @@ def scan(x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None, zoh=False
     backward pass (``scan_bwd(..., h_saved=...)``) starts from."""
     torch = _torch()
     lib = load_library()
-    if y is None:
-        odt = out_dtype if out_dtype is not None else x.dtype
-        y = torch.empty(x.shape, dtype=odt, device=x.device)
-    if h_last is None and want_h_last:
-        h_last = torch.empty((x.shape[0], x.shape[2], A.shape[1]), dtype=torch.float32,
-                             device=x.device)
-    args = make_scan_args(x, delta, A, B, C, D, h0, h_last, y, conv_w, conv_b, zoh, chunk_len,
-                          delta_bias, delta_softplus, z, conv_state_in, conv_state_out, h_saved)
-    need = int(lib.ssm_scan_workspace_size(ctypes.byref(args)))
-    if need > 0:
-        if workspace is None or workspace.numel() < need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-        args.workspace = _ptr(workspace)
-        args.workspace_bytes = workspace.numel()
-    if events is not None:
-        args.ev_main_start, args.ev_main_stop = events
-    status = lib.ssm_scan_fwd(ctypes.byref(args), _stream_handle(stream))
+    with _on_stream(stream):
+        if y is None:
+            odt = out_dtype if out_dtype is not None else x.dtype
+            y = torch.empty(x.shape, dtype=odt, device=x.device)
+        if h_last is None and want_h_last:
+            h_last = torch.empty((x.shape[0], x.shape[2], A.shape[1]), dtype=torch.float32,
+                                 device=x.device)
+        args = make_scan_args(x, delta, A, B, C, D, h0, h_last, y, conv_w, conv_b, zoh,
+                              chunk_len, delta_bias, delta_softplus, z, conv_state_in,
+                              conv_state_out, h_saved)
+        need = int(lib.ssm_scan_workspace_size(ctypes.byref(args)))
+        if need > 0:
+            if workspace is None or workspace.numel() < need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            args.workspace = _ptr(workspace)
+            args.workspace_bytes = workspace.numel()
+        if events is not None:
+            args.ev_main_start, args.ev_main_stop = events
+        status = lib.ssm_scan_fwd(ctypes.byref(args), _stream_handle(stream))
     _raise_for(lib, status)
     return y, h_last
 
@@ -347,7 +361,10 @@ class PreparedScan:
     """A scan whose arguments are validated and marshalled once, for callers
     that run the same shapes and buffers repeatedly (a decode loop, a
     benchmark, stream capture).  ``run()`` only launches; the tensors passed
-    to ``prepare_scan`` must stay alive and unchanged in place/shape."""
+    to ``prepare_scan`` must stay alive and unchanged in place/shape.  The
+    object keeps the outputs and workspace it allocated alive; when it has
+    run on a stream other than the one it was prepared on, synchronize that
+    stream before dropping it."""
 
     def __init__(self, args: ScanArgs, keep: tuple):
         self.args = args
@@ -465,12 +482,13 @@ def step(h, x, delta, A, B, C, D=None, zoh=False, y=None, out_dtype=None, stream
     Returns y (batch, dim)."""
     torch = _torch()
     lib = load_library()
-    if y is None:
-        y = torch.empty(x.shape, dtype=out_dtype if out_dtype is not None else x.dtype,
-                        device=x.device)
-    args = make_step_args(h, x, delta, A, B, C, D, y, zoh, delta_bias, delta_softplus, z,
-                          conv_w, conv_b, conv_state)
-    status = lib.ssm_step(ctypes.byref(args), _stream_handle(stream))
+    with _on_stream(stream):
+        if y is None:
+            y = torch.empty(x.shape, dtype=out_dtype if out_dtype is not None else x.dtype,
+                            device=x.device)
+        args = make_step_args(h, x, delta, A, B, C, D, y, zoh, delta_bias, delta_softplus, z,
+                              conv_w, conv_b, conv_state)
+        status = lib.ssm_step(ctypes.byref(args), _stream_handle(stream))
     _raise_for(lib, status)
     return y
 
@@ -576,14 +594,16 @@ def scan_bwd(x, delta, A, B, C, dy, D=None, h0=None, dh_last=None, zoh=False, wa
     torch = _torch()
     lib = load_library()
     dev = x.device
-    g = _bwd_outputs(x, A, want_dD, want_dh0)
-    args = make_bwd_args(x, delta, A, B, C, dy, D, h0, dh_last, zoh, g, super_chunk, h_saved)
-    need = int(lib.ssm_scan_bwd_workspace_size(ctypes.byref(args)))
-    if need > 0:
-        if workspace is None or workspace.numel() < need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-        args.workspace = _ptr(workspace)
-        args.workspace_bytes = workspace.numel()
-    status = lib.ssm_scan_bwd(ctypes.byref(args), _stream_handle(stream))
+    with _on_stream(stream):
+        g = _bwd_outputs(x, A, want_dD, want_dh0)
+        args = make_bwd_args(x, delta, A, B, C, dy, D, h0, dh_last, zoh, g, super_chunk,
+                             h_saved)
+        need = int(lib.ssm_scan_bwd_workspace_size(ctypes.byref(args)))
+        if need > 0:
+            if workspace is None or workspace.numel() < need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            args.workspace = _ptr(workspace)
+            args.workspace_bytes = workspace.numel()
+        status = lib.ssm_scan_bwd(ctypes.byref(args), _stream_handle(stream))
     _raise_for(lib, status)
     return {k: v for k, v in g.items() if v is not None}

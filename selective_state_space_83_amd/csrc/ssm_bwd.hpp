@@ -132,8 +132,11 @@ __device__ __forceinline__ void bwd_lane_step(float (&g)[NS], float (&dA)[NS],
     G[n] = fmaf(Cv[n], dyv, g[n]);
   }
   if (exact) {
+    // (the expm1 form only where the decay is weak: G + expm1 G cancels for
+    // a strong one, see decay_add)
 #pragma unroll
-    for (int n = 0; n < NS; ++n) ag[n] = fmaf(expm1_from(z2[n], a[n]), G[n], G[n]);
+    for (int n = 0; n < NS; ++n)
+      ag[n] = (a[n] > 0.5f) ? fmaf(expm1_from(z2[n], a[n]), G[n], G[n]) : a[n] * G[n];
   } else {
 #pragma unroll
     for (int n = 0; n < NS; ++n) ag[n] = a[n] * G[n];
@@ -251,7 +254,8 @@ k_bwd_summary(const BwdParams p) {
       for (int n = 0; n < N; ++n) {
         const float z2 = dv * cc.A2[n];
         const float G = fmaf(Ccur[n], dyv, g[n]);
-        g[n] = fmaf(expm1_from(z2, exp2_fast(z2)), G, G);
+        const float a = exp2_fast(z2);
+        g[n] = (a > 0.5f) ? fmaf(expm1_from(z2, a), G, G) : a * G;
       }
     } else {
 #pragma unroll
@@ -327,7 +331,7 @@ __global__ void __launch_bounds__(kWave) k_bwd_combine(const BwdParams p) {
   for (int64_t s = nc; s >= 1; --s) {
     const int64_t slot = b * nc + (s - 1);
     const float z2 = a2 * p.dsum_s[slot * p.D + d];
-    carry = fmaf(expm1_from(z2, exp2_fast(z2)), carry, carry + p.gsum[slot * DN + dn]);
+    carry = decay_add(z2, carry, p.gsum[slot * DN + dn]);
     p.gsum[slot * DN + dn] = carry;
   }
 }

@@ -45,7 +45,10 @@
 // and with a steady Delta that bias compounds over the whole memory horizon.
 // At any step where some lane has min_n |Delta A[n]| below a threshold, the
 // wave instead carries the decay as e = expm1(Delta A), evaluated by its
-// series for small arguments:  h' = h + e h + Bbar u.
+// series for small arguments:  h' = h + e h + Bbar u.  That form is used only
+// where Abar > 1/2: for a strong decay h + e h cancels, leaving a rounding
+// error of the size of the old h rather than of Abar h, so there the decay is
+// applied directly (Abar h + Bbar u) -- in the same wave, per state.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -272,7 +275,7 @@ __device__ __forceinline__ float ssm_step_lane(float (&h)[N], const ChanConst<N,
       } else {
         gu = (cc.invA[n] != 0.0f) ? (e * cc.invA[n]) * u : du;   // A = 0: limit Delta
       }
-      h[n] = fmaf(e, h[n], fmaf(gu, Bv[n], h[n]));
+      h[n] = (a > 0.5f) ? fmaf(e, h[n], fmaf(gu, Bv[n], h[n])) : fmaf(a, h[n], gu * Bv[n]);
     }
     if constexpr (WITH_Y) {
       if (n & 1) acc1 = fmaf(Cv[n], h[n], acc1);
@@ -652,9 +655,12 @@ k_chunk_summary(const ScanParams p) {
 }
 
 // exp(z) * carry + b with z2 = z * log2(e), keeping the decay accurate when
-// exp(z) is close to 1 (carry + expm1(z) carry + b).
+// exp(z) is close to 1 (carry + expm1(z) carry + b), and applied directly
+// when it is not (where carry + expm1(z) carry would cancel, leaving a
+// rounding error of the size of the carry itself).
 __device__ __forceinline__ float decay_add(float z2, float carry, float b) {
-  return fmaf(expm1_from(z2, exp2_fast(z2)), carry, carry + b);
+  const float a = exp2_fast(z2);
+  return (a > 0.5f) ? fmaf(expm1_from(z2, a), carry, carry + b) : fmaf(a, carry, b);
 }
 
 // Exclusive walk over G groups: vals[g] (a group's end state from zero) is

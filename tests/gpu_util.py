@@ -74,6 +74,97 @@ def compare(got, ref, tol, what=""):
     return rep
 
 
+# Gradient tolerance: every entry g of a gradient is a sum of chain-rule terms
+# (the adjoint itself being such a sum over later steps).  Its rounding error,
+# in any evaluation order and precision with unit roundoff u, is at most about
+# (depth * u) times the entry's magnitude -- the same sum with every quantity
+# replaced by its absolute value, which the oracle returns beside the
+# gradient.  So each entry is compared as
+#     |gpu - ref| <= rtol * magnitude
+# with rtol the forward tolerance of the input precision: an entry that
+# cancels to near zero is held to the size of its own terms, not to the
+# largest entry of the tensor.
+GRAD_RTOL = {"f32": 2e-4, "bf16": 2e-2}
+GRADS = ("dx", "ddelta", "dA", "dB", "dC", "dD", "dh0")
+
+
+def compare_grad(got, ref, mag, idt, what=""):
+    """Elementwise |got - ref| <= rtol * mag (+ 1e-30 for entries whose terms
+    are all exactly zero); returns the report dict."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    mag = np.asarray(mag, dtype=np.float64)
+    assert got.shape == ref.shape == mag.shape, (what, got.shape, ref.shape, mag.shape)
+    r = GRAD_RTOL[idt]
+    err = np.abs(got - ref)
+    bound = r * mag + 1e-30
+    bad = ~(err <= bound)
+    rep = dict(what=what, n=int(ref.size), failing=int(bad.sum()),
+               max_abs=float(err.max()) if err.size else 0.0,
+               max_err_over_mag=float((err / np.maximum(mag, 1e-300)).max()) if err.size else 0.0)
+    if rep["failing"]:
+        idx = np.argwhere(bad)[:5]
+        samples = [(tuple(int(v) for v in i), float(got[tuple(i)]), float(ref[tuple(i)]),
+                    float(mag[tuple(i)])) for i in idx]
+        raise AssertionError("%s: %d of %d outside rtol %g x magnitude; max err/mag %.3e; "
+                             "first (index, gpu, ref, magnitude) %s"
+                             % (what, rep["failing"], rep["n"], r, rep["max_err_over_mag"],
+                                samples))
+    return rep
+
+
+def oracle_bwd(inp, dy, dh_last=None, D=None, h0=None, zoh=False):
+    """The oracle's gradients and per-entry magnitudes (two dicts)."""
+    import oracle
+    return oracle.default().scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
+                                     D=D, h0=h0, dh_last=dh_last, zoh=zoh, nthreads=threads(),
+                                     mag=True)
+
+
+def oracle_bwd_channel_blocks(inp, dy, dh_last, D, h0, zoh=False, block=32):
+    """oracle_bwd for a one-row batch, run as independent channel blocks on the
+    host's threads (the oracle itself threads over batch rows only).  Every
+    per-channel gradient (dx, dDelta, dA, dD, dh0) of a block depends on that
+    block's channels alone; dB and dC sum over channels, so the blocks' fp64
+    partial sums (and magnitudes) are added, a reassociation far below the
+    tolerances."""
+    import concurrent.futures
+    import oracle
+    orc = oracle.default()
+    Bt, L, Dm = inp["x"].shape
+    assert Bt == 1
+    starts = list(range(0, Dm, block))
+
+    def one(d0):
+        ds = slice(d0, min(Dm, d0 + block))
+        sub = channel_slice(inp, 0, ds)
+        return d0, orc.scan_bwd(sub["x"], sub["delta"], sub["A"], sub["B"], sub["C"],
+                                np.ascontiguousarray(dy[:, :, ds]),
+                                D=None if D is None else np.ascontiguousarray(D[ds]),
+                                h0=None if h0 is None else np.ascontiguousarray(h0[:, ds]),
+                                dh_last=None if dh_last is None else
+                                np.ascontiguousarray(dh_last[:, ds]),
+                                zoh=zoh, nthreads=1, mag=True)
+
+    N = inp["A"].shape[1]
+    shapes = {"dx": (1, L, Dm), "ddelta": (1, L, Dm), "dA": (Dm, N), "dB": (1, L, N),
+              "dC": (1, L, N), "dD": (Dm,), "dh0": (1, Dm, N)}
+    g = {k: np.zeros(v) for k, v in shapes.items()}
+    m = {k: np.zeros(v) for k, v in shapes.items()}
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads()) as ex:
+        for d0, (gb, mb) in ex.map(one, starts):
+            ds = slice(d0, min(Dm, d0 + block))
+            for out, part in ((g, gb), (m, mb)):
+                out["dx"][:, :, ds] = part["dx"]
+                out["ddelta"][:, :, ds] = part["ddelta"]
+                out["dA"][ds] = part["dA"]
+                out["dD"][ds] = part["dD"]
+                out["dh0"][:, ds] = part["dh0"]
+                out["dB"] += part["dB"]
+                out["dC"] += part["dC"]
+    return g, m
+
+
 def gpu_scan(inp, in_dtype, out_dtype, zoh=False, chunk_len=0, h0=True, want_h_last=True):
     """Run the library on numpy inputs; returns (y, h_last) as float64 numpy."""
     import torch

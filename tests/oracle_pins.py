@@ -734,6 +734,66 @@ def pin_bwd_homogeneity(orc):
         assert abs((g0["dB"] * w["B"]).sum() - (loss0 - skip)) <= 1e-11 * max(1.0, abs(loss0))
 
 
+def _abs_problem(v, dy, dhl):
+    return ({k: np.abs(a) for k, a in v.items()}, np.abs(dy), np.abs(dhl))
+
+
+def pin_bwd_magnitude_is_abs_problem(orc):
+    """The per-entry magnitude of a gradient is its chain-rule sum with every
+    quantity replaced by its absolute value.  Where every term of a gradient
+    is a product of the inputs, the states and the adjoints with nonnegative
+    factors only (dx, dB, dC, dD, dh0 for both discretizations, and dA for
+    Delta*B, whose A-factor derivative is 0), that is exactly the gradient of
+    the same problem with every input replaced by its absolute value: the
+    states and adjoints of that problem are the magnitudes of the signed one.
+    The gradients returned beside the magnitudes are the plain ones, bit for
+    bit."""
+    rng = _rng(132)
+    Bt, L, D, N = 2, 40, 3, 4
+    for zoh in (False, True):
+        v = _bwd_problem(rng, Bt, L, D, N)
+        if zoh:
+            v["A"][2, 1] = 0.0
+        dy = rng.standard_normal((Bt, L, D))
+        dhl = rng.standard_normal((Bt, D, N))
+        args = (v["x"], v["delta"], v["A"], v["B"], v["C"], dy)
+        kw = dict(D=v["D"], h0=v["h0"], dh_last=dhl, zoh=zoh)
+        g, m = orc.scan_bwd(*args, mag=True, **kw)
+        g_plain = orc.scan_bwd(*args, **kw)
+        for k in g:
+            assert np.array_equal(g[k], g_plain[k]), k
+        a, ady, adhl = _abs_problem(v, dy, dhl)
+        a["A"] = v["A"]            # the decay exp(Delta A) keeps its sign
+        ga = orc.scan_bwd(a["x"], a["delta"], a["A"], a["B"], a["C"], ady, D=a["D"],
+                          h0=a["h0"], dh_last=adhl, zoh=zoh)
+        keys = ["dx", "dB", "dC", "dD", "dh0"] + ([] if zoh else ["dA"])
+        for k in keys:
+            _rel_close(m[k], ga[k], 1e-12, "magnitude %s zoh=%d" % (k, zoh))
+
+
+def pin_bwd_magnitude_bounds(orc):
+    """Every magnitude bounds its gradient from above (triangle inequality),
+    for signed inputs in both discretizations; and dDelta's magnitude equals
+    |dDelta| when x = 0 and h0, C, dy, dh_last are nonnegative, since every
+    term is then A * Abar * h_{t-1} times a nonnegative adjoint (A < 0)."""
+    rng = _rng(133)
+    Bt, L, D, N = 2, 60, 3, 4
+    for zoh in (False, True):
+        v = _bwd_problem(rng, Bt, L, D, N)
+        dy = rng.standard_normal((Bt, L, D))
+        dhl = rng.standard_normal((Bt, D, N))
+        g, m = orc.scan_bwd(v["x"], v["delta"], v["A"], v["B"], v["C"], dy, D=v["D"],
+                            h0=v["h0"], dh_last=dhl, zoh=zoh, mag=True)
+        for k in g:
+            assert np.all(np.abs(g[k]) <= m[k] * (1 + 1e-12) + 1e-300), (k, zoh)
+            assert np.all(m[k] >= 0.0), (k, zoh)
+        w = dict(v, x=np.zeros_like(v["x"]), h0=np.abs(v["h0"]), C=np.abs(v["C"]))
+        g, m = orc.scan_bwd(w["x"], w["delta"], w["A"], w["B"], w["C"], np.abs(dy), D=w["D"],
+                            h0=w["h0"], dh_last=np.abs(dhl), zoh=zoh, mag=True)
+        assert np.all(g["ddelta"] <= 0.0)
+        _rel_close(m["ddelta"], np.abs(g["ddelta"]), 1e-12, "magnitude ddelta zoh=%d" % zoh)
+
+
 ALL_PINS = [
     pin_hand_expansion_lti, pin_hand_expansion_selective, pin_lti_kernel,
     pin_lti_steady_state, pin_brute_force, pin_split_invariance,
@@ -742,4 +802,5 @@ ALL_PINS = [
     pin_conv_numpy, pin_conv_scan_brute, pin_softplus_delta, pin_softplus_values, pin_gate,
     pin_conv_state_window, pin_conv_state_prefix, pin_conv_split_invariance,
     pin_decode_conv_equals_scan, pin_bwd_finite_differences, pin_bwd_homogeneity,
+    pin_bwd_magnitude_is_abs_problem, pin_bwd_magnitude_bounds,
 ]

@@ -10,9 +10,11 @@ Small shapes span several 64-channel tiles, ragged tails and forced chunk
 plans (including chunks shorter than the conv window); a sequence split
 across calls and a prefill handed to decode steps are compared with one
 oracle scan of the whole sequence.  Each workload the bench runs with fused
-steps is checked at full size in the bench's launch configuration: conv and
-fp32 element by element, long on sampled channels, decode (512 tokens) on
-sampled channels token by token.
+steps is checked at full size in the bench's launch configuration, element
+by element: conv and fp32 directly, long with the oracle on channel blocks,
+decode (512 tokens) token by token over the whole batch.  Step-size
+pre-activations far out in both tails of softplus (+-20, +-40, +-80) are
+checked in the scan and in the decode step.
 """
 from __future__ import annotations
 
@@ -253,32 +255,36 @@ def test_workload_fp32_fused_full():
           G.compare(hl, h_ref, G.TOL["f32"], "fp32 fused h_last"))
 
 
-def test_workload_long_fused_sampled():
+def test_workload_long_fused_full():
     """The long workload (1 x 2^20 x 512 x 16, bf16) at full size with the
-    fused steps of its bench run; the oracle runs on sampled channels, whose
-    outputs depend on their own inputs and the shared B, C only."""
+    fused steps of its bench run: every y and h_last entry against the
+    oracle, run on 64-channel blocks (a channel's outputs depend on its own
+    inputs and the shared B, C only)."""
     w = SI.WORKLOADS["long"]
     inp = SI.scan_inputs(w)
     ex = SI.fused_inputs(w)
     G.say("workload long, fused", w)
     y, hl, _ = G.gpu_scan_fused(inp, ex, BENCH_SCAN_FUSED, w.in_dtype, w.out_dtype, zoh=w.zoh,
                                 h0=False)
-    ds = [0, 1, 63, 64, 300, 511]
-    sub = G.channel_slice(inp, 0, ds)
-    sub_ex = {"delta_raw": np.ascontiguousarray(ex["delta_raw"][0:1, :, ds]),
-              "z": np.ascontiguousarray(ex["z"][0:1, :, ds]),
-              "delta_bias": np.ascontiguousarray(ex["delta_bias"][ds])}
-    y_ref, h_ref, _ = G.oracle_scan_fused(sub, sub_ex, BENCH_SCAN_FUSED, zoh=w.zoh, h0=False)
-    G.say(G.compare(y[:, :, ds], y_ref, G.TOL["bf16"], "long fused y (sampled channels)"),
-          G.compare(hl[:, ds], h_ref, G.TOL["bf16"], "long fused h_last (sampled channels)"))
+    for d0 in range(0, w.dim, 64):
+        ds = slice(d0, min(w.dim, d0 + 64))
+        sub = G.channel_slice(inp, 0, ds)
+        sub_ex = {"delta_raw": np.ascontiguousarray(ex["delta_raw"][0:1, :, ds]),
+                  "z": np.ascontiguousarray(ex["z"][0:1, :, ds]),
+                  "delta_bias": np.ascontiguousarray(ex["delta_bias"][ds])}
+        y_ref, h_ref, _ = G.oracle_scan_fused(sub, sub_ex, BENCH_SCAN_FUSED, zoh=w.zoh,
+                                              h0=False)
+        G.compare(y[:, :, ds], y_ref, G.TOL["bf16"], "long fused y channels %d.." % d0)
+        G.compare(hl[:, ds], h_ref, G.TOL["bf16"], "long fused h_last channels %d.." % d0)
 
 
-def test_workload_decode_fused_sampled():
+def test_workload_decode_fused_full():
     """512 consecutive ssm_step calls on (256, 5120, 16) with the fused steps
     of the decode bench run (softplus step size with bias, output gate, a
-    4-tap conv over the rolling window), state and window updated in place;
-    sampled channels checked token by token against the oracle's decode step,
-    the window exactly."""
+    4-tap conv over the rolling window), state and window updated in place:
+    every channel's y at every token against the oracle's decode step run
+    token by token over the whole batch, then the final state, and the final
+    window exactly."""
     w = SI.WORKLOADS["decode"]
     n = w.steps
     inp = SI.decode_inputs(w)
@@ -296,23 +302,88 @@ def test_workload_decode_fused_sampled():
                  delta_softplus=True, z=zs[s], conv_w=cw, conv_b=cb, conv_state=cs)
     torch.cuda.synchronize()
     y, h_fin, cs_fin = G.host(ys), h.cpu().numpy(), cs.cpu().numpy()
+    del ys, xs, drs, zs
+    torch.cuda.empty_cache()
     orc = oracle.default()
     tol = G.TOL["bf16"]
-    rng = np.random.default_rng(8)
-    for b in [0, 1, 255] + list(rng.integers(0, w.batch, 2)):
-        ds = sorted(set([0, 63, 64, 5119] + list(rng.integers(0, w.dim, 4))))
-        sl = lambda a: np.ascontiguousarray(a[b:b + 1][:, ds])
-        hr = sl(inp["h"]).astype(np.float64)
-        csr = sl(ex["conv_state"]).astype(np.float64)
-        for s in range(n):
-            yr, hr, csr = orc.step(hr, sl(inp["x"][s]), sl(ex["delta_raw"][s]), inp["A"][ds],
-                                   inp["B"][s][b:b + 1], inp["C"][s][b:b + 1], inp["D"][ds],
-                                   delta_bias=ex["delta_bias"][ds], delta_softplus=True,
-                                   z=sl(ex["z"][s]), conv_w=ex["conv_w"][ds],
-                                   conv_b=ex["conv_b"][ds], conv_state=csr)
-            G.compare(y[s][b:b + 1][:, ds], yr, tol, "fused decode y step %d b=%d" % (s, b))
-        G.compare(sl(h_fin), hr, tol, "fused decode h b=%d" % b)
-        assert np.array_equal(sl(cs_fin), csr.astype(np.float32)), "fused decode window b=%d" % b
+    hr, csr = inp["h"], ex["conv_state"]
+    for s in range(n):
+        yr, hr, csr = orc.step(hr, inp["x"][s], ex["delta_raw"][s], inp["A"], inp["B"][s],
+                               inp["C"][s], inp["D"], delta_bias=ex["delta_bias"],
+                               delta_softplus=True, z=ex["z"][s], conv_w=ex["conv_w"],
+                               conv_b=ex["conv_b"], conv_state=csr, nthreads=G.threads())
+        G.compare(y[s], yr, tol, "fused decode y token %d" % s)
+    G.compare(h_fin, hr, tol, "fused decode final h")
+    assert np.array_equal(cs_fin, csr.astype(np.float32)), "fused decode window"
+
+
+# step-size pre-activations far into both tails of softplus: softplus(v) is v
+# itself to fp32 precision above about 17 and exp(v) below about -17 (both
+# discretizations; +80 makes exp(Delta A) underflow to 0)
+TAILS = np.array([-80.0, -40.0, -20.0, 20.0, 40.0, 80.0], dtype=np.float32)
+
+
+def _tail_preactivations(raw, rng):
+    """raw with blocks of steps and channels set to the tail values (the rest
+    keeps the workload's recipe)."""
+    raw = raw.copy()
+    L, D = raw.shape[-2], raw.shape[-1]
+    for k, v in enumerate(TAILS):
+        t0 = (k * L) // len(TAILS)
+        span = max(1, L // (3 * len(TAILS)))
+        raw[..., t0:t0 + span, k::3] = v
+    idx = rng.integers(0, raw.size, size=max(1, raw.size // 50))
+    raw.reshape(-1)[idx] = rng.choice(TAILS, size=idx.size)
+    return raw
+
+
+@pytest.mark.parametrize("idt", ["f32", "bf16"])
+@pytest.mark.parametrize("zoh", [False, True])
+def test_softplus_tails_scan(idt, zoh):
+    """Scan with the softplus step size whose pre-activations reach +-20,
+    +-40 and +-80 (bias 0), unchunked and chunked, against the oracle."""
+    Bt, L, D, N = 2, 600, 130, 16
+    w = SI.Workload("tails", 70, Bt, L, D, N, idt, "f32", zoh=zoh, a_dist="random",
+                    dskip_dist="uniform")
+    inp = SI.scan_inputs(w, seed=2100 + 2 * int(zoh) + (idt == "bf16"), h0=True)
+    ex = SI.fused_inputs(w)
+    rng = np.random.default_rng(2200)
+    ex["delta_raw"] = SI._store(_tail_preactivations(ex["delta_raw"], rng), idt)
+    ex["delta_bias"] = np.zeros(D, dtype=np.float32)
+    use = {"softplus", "gate"}
+    y_ref, h_ref, _ = G.oracle_scan_fused(inp, ex, use, zoh=zoh, h0=True)
+    for cl in (0, 48, L):
+        G.say("tails", idt, zoh, "chunk_len", cl)
+        y, hl, _ = G.gpu_scan_fused(inp, ex, use, idt, "f32", zoh=zoh, chunk_len=cl, h0=True)
+        G.compare(y, y_ref, G.TOL[idt], "tails y cl=%d" % cl)
+        G.compare(hl, h_ref, G.TOL[idt], "tails h_last cl=%d" % cl)
+
+
+@pytest.mark.parametrize("zoh", [False, True])
+def test_softplus_tails_step(zoh):
+    """Decode steps whose step-size pre-activations reach +-20, +-40, +-80."""
+    Bt, D, N, idt = 6, 130, 16, "f32"
+    steps = 12
+    w = SI.Workload("tailstep", 71, Bt, steps, D, N, idt, idt, zoh=zoh, a_dist="random",
+                    dskip_dist="uniform")
+    inp = SI.scan_inputs(w, seed=2300 + int(zoh), h0=True)
+    rng = np.random.default_rng(2301)
+    raw = _tail_preactivations(0.5 * rng.standard_normal((Bt, steps, D)).astype(np.float32),
+                               rng)
+    h = G.dev(inp["h0"])
+    hr = inp["h0"].astype(np.float64)
+    A, Dv = G.dev(inp["A"]), G.dev(inp["D"])
+    zero = np.zeros(D, dtype=np.float32)
+    orc = oracle.default()
+    for t in range(steps):
+        dl = np.ascontiguousarray(raw[:, t])
+        yt = ssm.step(h, G.dev(inp["x"][:, t]), G.dev(dl), A, G.dev(inp["B"][:, t]),
+                      G.dev(inp["C"][:, t]), Dv, zoh=zoh, delta_bias=G.dev(zero),
+                      delta_softplus=True)
+        yr, hr = orc.step(hr, inp["x"][:, t], dl, inp["A"], inp["B"][:, t], inp["C"][:, t],
+                          inp["D"], zoh=zoh, delta_bias=zero, delta_softplus=True)
+        G.compare(G.host(yt), yr, G.TOL[idt], "tail step %d y" % t)
+        G.compare(h.cpu().numpy(), hr, G.TOL[idt], "tail step %d h" % t)
 
 
 def _canaried(shape, dtype, pad, canary):

@@ -4,8 +4,10 @@ binding.  Every test needs an MI355X.
 
 Sizes: small shapes spanning several 64-channel tiles, ragged tails and
 forced chunkings are compared element by element; the five task workloads run
-at full size in the launch configuration the benchmark times, compared in
-full where the oracle finishes in seconds and on sampled channels otherwise.
+at full size in the launch configuration the benchmark times and are compared
+element by element too (the long scan with the oracle on channel blocks, the
+512-token decode token by token); quicker sampled checks of the long and
+decode workloads run beside them.
 """
 from __future__ import annotations
 
@@ -143,6 +145,25 @@ def test_workload_long_sampled():
     _sampled_channels(inp, w, y, hl, [(0, ds)])
 
 
+def test_workload_long_full():
+    """The long workload (batch 1, L 2^20, D 512, N 16, bf16 in and out) in the
+    bench's launch configuration: every y and every h_last entry compared
+    with the oracle, which runs on 64-channel blocks (B and C shared) so the
+    host holds one block's fp64 arrays at a time."""
+    w = SI.WORKLOADS["long"]
+    G.say("workload long (full comparison)", w)
+    inp = SI.scan_inputs(w)
+    y, hl = G.gpu_scan(inp, w.in_dtype, w.out_dtype, h0=False)
+    tol = G.TOL[w.in_dtype]
+    for d0 in range(0, w.dim, 64):
+        ds = slice(d0, min(w.dim, d0 + 64))
+        sub = G.channel_slice(inp, 0, ds)
+        y_ref, h_ref = G.oracle_scan(sub, zoh=w.zoh, h0=False)
+        G.compare(y[:, :, ds], y_ref, tol, "long y channels %d.." % d0)
+        G.compare(hl[:, ds], h_ref, tol, "long h_last channels %d.." % d0)
+    G.say("long: all %d outputs and %d states compared" % (y.size, hl.size))
+
+
 def test_workload_long_lti_closed_form():
     """LTI variant: Delta, B, C constant in time.  Sampled outputs are checked
     against y_t = sum_{j<=t} K_{t-j} x_j + D x_t with the kernel
@@ -213,6 +234,106 @@ def test_workload_decode_sampled():
                               inp["D"][ds])
             G.compare(y[s][b:b + 1][:, ds], yr, tol, "decode y step %d b=%d" % (s, b))
         G.compare(h_fin[b:b + 1][:, ds], hr, tol, "decode h b=%d" % b)
+
+
+def test_workload_decode_full():
+    """512 consecutive ssm_step calls on (256, 5120, 16), state updated in place
+    on the GPU: every channel's y at every one of the 512 tokens and the
+    final state compared with the oracle's decode step run token by token
+    over the whole batch."""
+    w = SI.WORKLOADS["decode"]
+    steps = w.steps
+    inp = SI.decode_inputs(w)
+    h = G.dev(inp["h"])
+    A, Dv = G.dev(inp["A"]), G.dev(inp["D"])
+    xs = G.dev(inp["x"], "bf16")
+    dls = G.dev(inp["delta"], "bf16")
+    Bs = G.dev(inp["B"], "bf16")
+    Cs = G.dev(inp["C"], "bf16")
+    ys = torch.empty((steps, w.batch, w.dim), dtype=torch.bfloat16, device="cuda")
+    calls = [ssm.prepare_step(h, xs[s], dls[s], A, Bs[s], Cs[s], Dv, y=ys[s])[0]
+             for s in range(steps)]
+    for c in calls:
+        c.run()
+    torch.cuda.synchronize()
+    y = G.host(ys)
+    h_fin = h.cpu().numpy()
+    del ys, xs, dls, calls
+    torch.cuda.empty_cache()
+    G.say("decode: gpu done, oracle token by token")
+    orc = oracle.default()
+    tol = G.TOL["bf16"]
+    hr = inp["h"]
+    for s in range(steps):
+        yr, hr = orc.step(hr, inp["x"][s], inp["delta"][s], inp["A"], inp["B"][s], inp["C"][s],
+                          inp["D"], nthreads=G.threads())
+        G.compare(y[s], yr, tol, "decode y token %d" % s)
+    G.compare(h_fin, hr, tol, "decode final h")
+    G.say("decode: all %d outputs and %d states compared" % (y.size, h_fin.size))
+
+
+def test_decode_equals_scan_512():
+    """512 ssm_step calls from h0 equal one scan of L = 512 from h0 (y at
+    every token and the final state), both discretizations; the scan splits
+    into chunks, so the decode's one-token updates are checked against the
+    chunked carries."""
+    for idt, zoh in (("f32", False), ("bf16", True)):
+        L = 512
+        w = SI.Workload("d512", 9, 3, L, 130, 16, idt, idt, zoh=zoh, a_dist="random",
+                        dskip_dist="uniform")
+        inp = SI.scan_inputs(w, seed=12, h0=True)
+        y_scan, h_scan = G.gpu_scan(inp, idt, idt, zoh=zoh, h0=True, chunk_len=48)
+        h = G.dev(inp["h0"])
+        A, Dv = G.dev(inp["A"]), G.dev(inp["D"])
+        t = {k: G.dev(np.ascontiguousarray(np.moveaxis(inp[k], 1, 0)), idt)
+             for k in ("x", "delta", "B", "C")}
+        ys = torch.empty((L,) + tuple(t["x"].shape[1:]), dtype=G.torch_dtype(idt),
+                         device="cuda")
+        for s in range(L):
+            ssm.step(h, t["x"][s], t["delta"][s], A, t["B"][s], t["C"][s], Dv, zoh=zoh,
+                     y=ys[s])
+        torch.cuda.synchronize()
+        tol = G.TOL[idt]
+        G.compare(np.moveaxis(G.host(ys), 0, 1), y_scan, tol, "decode x512 vs scan y " + idt)
+        G.compare(h.cpu().numpy(), h_scan, tol, "decode x512 vs scan h " + idt)
+        y_ref, h_ref = G.oracle_scan(inp, zoh=zoh, h0=True)
+        G.compare(y_scan, y_ref, tol, "scan y " + idt)
+
+
+def test_large_delta_underflow():
+    """Step sizes large enough that exp(Delta A) underflows to 0 (Delta up to
+    100 against |A| up to 8), next to ordinary ones, and within waves that
+    also hold tiny step sizes (the slow-decay form then runs beside a total
+    decay), for both discretizations, both input precisions and several
+    chunkings: y and h_last against the oracle.
+
+    With Delta*B the input term Delta B x grows with Delta, so x is divided by
+    Delta at those steps: the states keep their usual size, and outputs stay
+    well conditioned for the elementwise tolerance (a state 50 times larger
+    would leave outputs that cancel to a few thousandths with fp32 rounding
+    of the size of its terms, about 2^-24 times 50, beyond atol)."""
+    for idt in ("f32", "bf16"):
+        for zoh in (False, True):
+            w = SI.Workload("big", 13, 2, 700, 130, 16, idt, "f32", zoh=zoh, a_dist="random",
+                            dskip_dist="uniform")
+            inp = SI.scan_inputs(w, seed=31, h0=True)
+            dl = inp["delta"].copy()
+            dl[:, 100:110, :] = 50.0
+            dl[:, 300:305, ::3] = 100.0
+            dl[:, 500:520, 0::2] = 1e-6
+            dl[:, 500:520, 1::2] = 60.0
+            dl[:, 640:650, 5] = 20.0
+            inp["delta"] = SI._store(dl, idt)
+            if not zoh:
+                big = inp["delta"] > 1.0
+                inp["x"] = SI._store(np.where(big, inp["x"] / np.maximum(inp["delta"], 1.0),
+                                              inp["x"]), idt)
+            y_ref, h_ref = G.oracle_scan(inp, zoh=zoh, h0=True)
+            for cl in (0, 64, 37, 700):
+                G.say("large delta", idt, "zoh" if zoh else "delta_b", "chunk_len", cl)
+                y, hl = G.gpu_scan(inp, idt, "f32", zoh=zoh, chunk_len=cl, h0=True)
+                G.compare(y, y_ref, G.TOL[idt], "large delta y %s zoh=%d cl=%d" % (idt, zoh, cl))
+                G.compare(hl, h_ref, G.TOL[idt], "large delta h %s zoh=%d cl=%d" % (idt, zoh, cl))
 
 
 def test_long_memory_stress():
@@ -398,6 +519,37 @@ def test_no_writes_outside_outputs():
     assert torch.all(wbuf[:pad] == 0xA5) and torch.all(wbuf[-pad:] == 0xA5)
     y_ref, h_ref = G.oracle_scan(inp, h0=True)
     G.compare(G.host(y), y_ref, G.TOL["f32"], "canary y")
+
+
+def test_side_stream_workspace():
+    """A scan and a backward launched on a side stream allocate their outputs
+    and workspace on that stream: work queued on the current stream right
+    after the calls (allocations of the same sizes, filled with NaN) cannot
+    take the freed workspace while the side stream's kernels still use it."""
+    inp = _medium_inputs(L=4000, D=200)
+    t = {k: G.dev(v) for k, v in inp.items() if v is not None}
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    y, hl = ssm.scan(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], h0=t["h0"],
+                     chunk_len=50, stream=side)
+    args = ssm.make_scan_args(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["h0"], hl,
+                              y, chunk_len=50)
+    junk = [torch.full((ssm.workspace_size(args),), 255, dtype=torch.uint8, device="cuda")
+            for _ in range(4)]
+    dy = G.dev(np.random.default_rng(3).standard_normal(inp["x"].shape).astype(np.float32))
+    side.wait_stream(torch.cuda.current_stream())
+    g = ssm.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], dy, D=t["D"], h0=t["h0"],
+                     stream=side)
+    junk += [torch.full((1 << 26,), float("nan"), device="cuda") for _ in range(4)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    y_ref, h_ref = G.oracle_scan(inp, h0=True)
+    G.compare(G.host(y), y_ref, G.TOL["f32"], "side stream y")
+    G.compare(hl.cpu().numpy(), h_ref, G.TOL["f32"], "side stream h_last")
+    ref, mag = G.oracle_bwd(inp, dy.cpu().numpy(), D=inp["D"], h0=inp["h0"])
+    for k in G.GRADS:
+        G.compare_grad(g[k].cpu().numpy(), ref[k], mag[k], "f32", "side stream " + k)
 
 
 def test_empty_sequence_hands_back_h0():

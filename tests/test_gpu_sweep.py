@@ -186,13 +186,8 @@ def test_sweep_bwd(case):
     g = ssm.scan_bwd(t["x"], t["delta"], A, t["B"], t["C"], G.dev(gi["dy"], idt), D=G.dev(Dv),
                      h0=h0d, dh_last=G.dev(dh_last), zoh=zoh, super_chunk=sc, h_saved=hs)
     torch.cuda.synchronize()
-    ref = oracle.default().scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
-                                    gi["dy"], D=Dv, h0=inp.get("h0"), dh_last=dh_last, zoh=zoh,
-                                    nthreads=G.threads())
-    r = 2e-4 if idt == "f32" else 2e-2
-    for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dh0"):
-        if k not in g or ref.get(k) is None:
+    ref, mag = G.oracle_bwd(inp, gi["dy"], dh_last=dh_last, D=Dv, h0=inp.get("h0"), zoh=zoh)
+    for k in G.GRADS:
+        if k not in g:
             continue
-        want = np.asarray(ref[k], dtype=np.float64)
-        scale = float(np.abs(want).max()) if want.size else 0.0
-        G.compare(g[k].cpu().numpy(), want, dict(rtol=r, atol=r * scale + 1e-30), k)
+        G.compare_grad(g[k].cpu().numpy(), ref[k], mag[k], idt, k)

@@ -64,6 +64,17 @@ MUTANTS = [
     ("bwd_dD_no_input", "dD[d] += gy * u;", "dD[d] += gy;"),
     ("bwd_dh0_undecayed", "for (int64_t n = 0; n < N; ++n) p.dh0[(b * D + d) * N + n] = g[n];",
      "for (int64_t n = 0; n < N; ++n) p.dh0[(b * D + d) * N + n] = g[n] + 1e-3;"),
+    # the per-entry magnitudes that set the gradient tolerances
+    ("mag_adjoint_no_decay", "gm[n] = abar * Gm;", "gm[n] = Gm;"),
+    ("mag_drop_output_term", "const double Gm = gm[n] + std::fabs(Cn * gy);",
+     "const double Gm = gm[n];"),
+    ("mag_ddelta_signed_A",
+     "mddt += Gm * (std::fabs(a_cont) * abar * hpm + std::fabs(df_dt * Bn * u));",
+     "mddt += Gm * (a_cont * abar * hpm + std::fabs(df_dt * Bn * u));"),
+    ("mag_state_signed_input", "if (mag) Hm[(t + 1) * N + n] = abar * Hm[t * N + n] + std::fabs(inp);",
+     "if (mag) Hm[(t + 1) * N + n] = abar * Hm[t * N + n] + inp;"),
+    ("mag_dx_no_skip", "double mdu = std::fabs(dskip * gy), mddt = 0.0;",
+     "double mdu = 0.0, mddt = 0.0;"),
 ]
 
 
