@@ -65,7 +65,9 @@
  *              be 4-byte aligned and are best 64-byte aligned.
  *   Memory     every pointer is a DEVICE pointer owned by the caller.  The
  *              library allocates nothing, keeps no pointer after the call and
- *              holds no global mutable state; it is reentrant and thread-safe.
+ *              holds no global mutable state apart from the scratch array of
+ *              ssm_scan_fwd_noalloc and its per-device address table; every
+ *              entry point except that one is reentrant and thread-safe.
  *   Streams    hip_stream is a hipStream_t (NULL = the default stream).  Work
  *              is enqueued asynchronously; the call never synchronizes.  A
  *              call enqueues kernel launches only (plus the optional timing
@@ -232,6 +234,10 @@ typedef struct {
                                          delta, A, Bm, h0 (and disc); NULL = computed here */
 } ssm_scan_bwd_args_t;
 
+/* Bytes of device scratch the allocation-free forward entry point holds per
+ * GPU (see ssm_scan_fwd_noalloc). */
+#define SSM_NOALLOC_SCRATCH_BYTES (64u << 20)
+
 /* Returns SSM_ABI_VERSION. */
 int ssm_abi_version(void);
 
@@ -250,6 +256,30 @@ int64_t ssm_scan_plan_chunk_len(const ssm_scan_args_t* args);
  *   (a, b) o (a', b') = (a a', a' b + b')
  * which is exact up to floating-point rounding order. */
 ssm_status_t ssm_scan_fwd(const ssm_scan_args_t* args, void* hip_stream);
+
+/* ssm_scan_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops, and harnesses that forbid hipMalloc.
+ * Same arguments and results as ssm_scan_fwd, except that workspace and
+ * workspace_bytes are ignored: the chunk summaries, carries and group
+ * carries live in a device array of SSM_NOALLOC_SCRATCH_BYTES that the
+ * library keeps on every GPU it runs on, until the process ends.  The call
+ * allocates nothing.
+ *   - Plan: the library's plan when its summaries fit the array; otherwise
+ *     the same plan with chunks lengthened until they do (results then
+ *     differ from ssm_scan_fwd's by rounding order only).  A chunk_len the
+ *     caller forces is kept, and the call fails with SSM_ERR_WORKSPACE if
+ *     its summaries do not fit.  ssm_scan_plan_chunk_len reports the
+ *     ordinary plan, not this one.
+ *   - The array's device address is looked up (hipGetSymbolAddress) on the
+ *     first call on each device that needs it, with that device current;
+ *     make that first call outside stream capture.  hip_stream must belong
+ *     to the current device (SSM_ERR_UNSUPPORTED otherwise).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (concurrent streams, or threads) race and corrupt each
+ *     other's results.  Serialize them, e.g. on one stream.  Nothing in the
+ *     array needs clearing between calls; it keeps the last call's contents.
+ * Errors as for ssm_scan_fwd. */
+ssm_status_t ssm_scan_fwd_noalloc(const ssm_scan_args_t* args, void* hip_stream);
 
 /* One recurrent decode step per sequence: u = x (or the conv over the
  * window conv_state followed by x, then SiLU), h <- Abar h + Bbar u, then

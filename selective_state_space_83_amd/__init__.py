@@ -108,8 +108,11 @@ class BwdArgs(ctypes.Structure):
 
 
 EXPORTS = ["ssm_abi_version", "ssm_scan_workspace_size", "ssm_scan_plan_chunk_len",
-           "ssm_scan_fwd", "ssm_step", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd",
-           "ssm_status_string", "ssm_last_error_message"]
+           "ssm_scan_fwd", "ssm_scan_fwd_noalloc", "ssm_step", "ssm_scan_bwd_workspace_size",
+           "ssm_scan_bwd", "ssm_status_string", "ssm_last_error_message"]
+
+# bytes of device scratch ssm_scan_fwd_noalloc keeps per GPU (SSM_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -131,6 +134,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssm_scan_plan_chunk_len.argtypes = [ctypes.POINTER(ScanArgs)]
     lib.ssm_scan_fwd.restype = ctypes.c_int
     lib.ssm_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), ctypes.c_void_p]
+    lib.ssm_scan_fwd_noalloc.restype = ctypes.c_int
+    lib.ssm_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ScanArgs), ctypes.c_void_p]
     lib.ssm_step.restype = ctypes.c_int
     lib.ssm_step.argtypes = [ctypes.POINTER(StepArgs), ctypes.c_void_p]
     lib.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
@@ -355,6 +360,15 @@ def scan(x, delta, A, B, C, D=None, h0=None, conv_w=None, conv_b=None, zoh=False
         status = lib.ssm_scan_fwd(ctypes.byref(args), _stream_handle(stream))
     _raise_for(lib, status)
     return y, h_last
+
+
+def scan_noalloc(args: ScanArgs, stream=None) -> None:
+    """ssm_scan_fwd_noalloc on arguments filled by ``make_scan_args`` (outputs
+    included): the forward scan with its chunk summaries in the library's
+    per-GPU scratch array, so neither this function nor the library
+    allocates.  Calls on one GPU must not overlap in time."""
+    lib = load_library()
+    _raise_for(lib, lib.ssm_scan_fwd_noalloc(ctypes.byref(args), _stream_handle(stream)))
 
 
 class PreparedScan:

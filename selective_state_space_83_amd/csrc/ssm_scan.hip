@@ -7,10 +7,19 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "ssm_scan.h"
 #include "ssm_kernels.hpp"
 #include "ssm_bwd.hpp"
+
+// Device scratch of the allocation-free forward entry point
+// (ssm_scan_fwd_noalloc): the chunk summaries, carries and group carries that
+// ssm_scan_fwd keeps in the caller's workspace.  One copy per GPU, held
+// until the process ends.  Host code never uses this name as an address: the
+// per-device address comes from hipGetSymbolAddress.
+constexpr size_t kNoallocScratchBytes = size_t(SSM_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -164,8 +173,27 @@ bool misaligned(const void* p, size_t align) {
   return p && (reinterpret_cast<uintptr_t>(p) % align) != 0;
 }
 
-// Validation common to the scan; fills the plan on success.
-ssm_status_t check_scan(const ssm_scan_args_t* a, Plan* plan) {
+// The plan of the allocation-free entry point: the library's plan when its
+// summaries fit the scratch array, otherwise the same plan with chunks
+// lengthened (by doubling, kept a multiple of 4) until they do; a chunk
+// length the caller forces is kept as given.
+Plan scratch_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t chunk_len) {
+  Plan pl = make_plan(Bt, L, D, N, chunk_len);
+  if (chunk_len > 0) return pl;
+  while (pl.ws_total > kNoallocScratchBytes && pl.C > 1) {
+    int64_t T = std::min<int64_t>(L, (2 * pl.T + kChunkAlign - 1) / kChunkAlign * kChunkAlign);
+    if (T > INT32_MAX) T = L;
+    const Plan next = make_plan(Bt, L, D, N, static_cast<int32_t>(std::min<int64_t>(T, INT32_MAX)));
+    if (next.T <= pl.T) break;   // capped (32-bit row offsets): cannot lengthen further
+    pl = next;
+  }
+  return pl;
+}
+
+// Validation common to the scan; fills the plan on success.  With
+// `own_scratch` (the allocation-free entry point) the plan must fit the
+// library's scratch array, and the caller's workspace fields are ignored.
+ssm_status_t check_scan(const ssm_scan_args_t* a, Plan* plan, bool own_scratch = false) {
   if (!a) return fail(SSM_ERR_NULL, "args is NULL");
   if (a->batch < 0 || a->seqlen < 0 || a->dim < 0)
     return fail(SSM_ERR_SHAPE, "negative size: batch=%lld seqlen=%lld dim=%lld",
@@ -196,7 +224,13 @@ ssm_status_t check_scan(const ssm_scan_args_t* a, Plan* plan) {
       !mul_ok(a->batch, dn, &bdn) || bld > INT64_MAX / 8 || bln > INT64_MAX / 8 ||
       bdn > INT64_MAX / 8 || !mul_ok(a->batch * a->dim, win, &bds) || bds > INT64_MAX / 8)
     return fail(SSM_ERR_SHAPE, "sizes overflow");
-  *plan = make_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len);
+  *plan = own_scratch ? scratch_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len)
+                     : make_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len);
+  if (own_scratch && plan->ws_total > kNoallocScratchBytes)
+    return fail(SSM_ERR_WORKSPACE,
+                "the chunk summaries of this plan need %zu bytes of scratch; the "
+                "allocation-free entry point holds %zu (pass chunk_len = 0, or a longer one)",
+                plan->ws_total, kNoallocScratchBytes);
   const Range cso{win > 0 ? a->conv_state_out : nullptr, size_t(bds) * 4};
   const Range csi{win > 0 ? a->conv_state_in : nullptr, size_t(bds) * 4};
   if (misaligned(a->conv_state_in, 4) || misaligned(a->conv_state_out, 4))
@@ -252,7 +286,7 @@ ssm_status_t check_scan(const ssm_scan_args_t* a, Plan* plan) {
     return fail(SSM_ERR_ALIAS, "conv_state_out overlaps an output");
   if (overlap(hsv, y) || overlap(hsv, hl) || overlap(hsv, cso))
     return fail(SSM_ERR_ALIAS, "h_saved overlaps an output");
-  if (plan->ws_total > 0) {
+  if (plan->ws_total > 0 && !own_scratch) {
     if (!a->workspace) return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required", plan->ws_total);
     if (a->workspace_bytes < plan->ws_total)
       return fail(SSM_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", a->workspace_bytes,
@@ -336,6 +370,37 @@ ssm_status_t check_step(const ssm_step_args_t* a) {
 float exact_threshold(int32_t disc, int32_t in_dtype) {
   if (disc == SSM_DISC_ZOH) return in_dtype == SSM_BF16 ? 1.0f / 8192.0f : 0.03f;
   return in_dtype == SSM_BF16 ? 1.0f / 8192.0f : 1.0f / 1024.0f;
+}
+
+// Per-device address of `scratch`, looked up with that device current on the
+// first allocation-free call that needs it.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+ssm_status_t scratch_address(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SSM_ERR_UNSUPPORTED, "device %d", dev);
+  if (s) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(s, &sdev);
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(SSM_ERR_UNSUPPORTED,
+                  "the stream belongs to device %d but device %d is current", sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SSM_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SSM_OK;
 }
 
 ssm_status_t launch_status(const char* what) {
@@ -756,11 +821,13 @@ int64_t ssm_scan_plan_chunk_len(const ssm_scan_args_t* a) {
   return make_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len).T;
 }
 
-ssm_status_t ssm_scan_fwd(const ssm_scan_args_t* a, void* hip_stream) {
-  g_msg[0] = '\0';
-  Plan pl;
-  if (ssm_status_t st = check_scan(a, &pl)) return st;
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+}  // extern "C"
+
+namespace {
+
+// The forward scan of checked arguments with plan `pl`, its chunk summaries
+// in `ws` (pl.ws_total bytes; unused when the plan has one chunk).
+ssm_status_t scan_fwd_run(const ssm_scan_args_t* a, const Plan& pl, void* ws, hipStream_t s) {
   const int64_t BD = a->batch * a->dim;
   if (BD == 0) return SSM_OK;
   if (a->seqlen == 0) {
@@ -791,10 +858,10 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_args_t* a, void* hip_stream) {
   kp.conv_w = a->conv_w;
   kp.conv_b = a->conv_w ? a->conv_b : nullptr;
   kp.conv_k = a->conv_w ? a->conv_k : 0;
-  kp.dsum = pl.C > 1 ? static_cast<float*>(a->workspace) : nullptr;
-  kp.hsum = pl.C > 1 ? reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pl.ws_dsum) : nullptr;
+  kp.dsum = pl.C > 1 ? static_cast<float*>(ws) : nullptr;
+  kp.hsum = pl.C > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + pl.ws_dsum) : nullptr;
   if (pl.grp.G > 0) {
-    char* wsb = static_cast<char*>(a->workspace);
+    char* wsb = static_cast<char*>(ws);
     kp.gS = reinterpret_cast<float*>(wsb + pl.ws_dsum + pl.ws_hsum);
     kp.gB = reinterpret_cast<float*>(wsb + pl.ws_dsum + pl.ws_hsum + pl.ws_gS);
   }
@@ -819,6 +886,29 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_args_t* a, void* hip_stream) {
     case 8: return dispatch_types<8>(a, kp, pl, s);
     default: return dispatch_types<16>(a, kp, pl, s);
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status_t ssm_scan_fwd(const ssm_scan_args_t* a, void* hip_stream) {
+  g_msg[0] = '\0';
+  Plan pl;
+  if (ssm_status_t st = check_scan(a, &pl)) return st;
+  return scan_fwd_run(a, pl, a->workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+ssm_status_t ssm_scan_fwd_noalloc(const ssm_scan_args_t* a, void* hip_stream) {
+  g_msg[0] = '\0';
+  Plan pl;
+  if (ssm_status_t st = check_scan(a, &pl, true)) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  void* ws = nullptr;
+  if (pl.ws_total > 0 && a->seqlen > 0 && a->batch * a->dim > 0) {
+    if (ssm_status_t st = scratch_address(s, &ws)) return st;
+  }
+  return scan_fwd_run(a, pl, ws, s);
 }
 
 ssm_status_t ssm_step(const ssm_step_args_t* a, void* hip_stream) {

@@ -616,3 +616,17 @@ def test_wrapper_refuses_cpu_tensors(lib):
         ssm.scan(x, x.clone(), A, B, B.clone(), y=torch.zeros(1, 4, 8), want_h_last=False)
     with pytest.raises(ValueError):
         ssm.make_scan_args(x, x, A, B[:, :, :8], B)
+
+
+def test_noalloc_refuses_plans_beyond_its_scratch(lib):
+    """ssm_scan_fwd_noalloc checks everything on the host before any HIP
+    call: bad arguments as ssm_scan_fwd does, and a forced chunk length whose
+    summaries exceed the library's scratch array (SSM_ERR_WORKSPACE)."""
+    a = valid_scan_args(batch=1, L=1 << 19, D=512, chunk_len=64)
+    assert lib.ssm_scan_workspace_size(ctypes.byref(a)) > ssm.NOALLOC_SCRATCH_BYTES
+    assert lib.ssm_scan_fwd_noalloc(ctypes.byref(a), None) == ssm.SSM_ERR_WORKSPACE
+    assert b"scratch" in lib.ssm_last_error_message()
+    assert lib.ssm_scan_fwd_noalloc(None, None) == ssm.SSM_ERR_NULL
+    a = valid_scan_args()
+    a.x = None
+    assert lib.ssm_scan_fwd_noalloc(ctypes.byref(a), None) == ssm.SSM_ERR_NULL

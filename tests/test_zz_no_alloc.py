@@ -1,0 +1,114 @@
+"""ssm_scan_fwd_noalloc, the allocation-free forward entry point, through the
+C ABI: on two calls in a row (the second smaller, reusing the same per-GPU
+scratch array), each compared with ssm_scan_fwd on the same arguments, bit
+for bit where the two share a plan and against the oracle at the input
+precision's tolerance; a problem whose ordinary plan does not fit the scratch
+array runs with longer chunks and still matches the oracle."""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import gpu_util as G
+import ssm_inputs as SI
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import selective_state_space_83_amd as ssm  # noqa: E402
+
+
+def _args(inp, idt, zoh, h0, chunk_len=0, conv=False):
+    t = {k: G.dev(inp[k], idt) for k in ("x", "delta", "B", "C")}
+    for k in ("A", "D", "conv_w", "conv_b"):
+        t[k] = G.dev(inp.get(k))
+    h0d = G.dev(inp["h0"]) if h0 else None
+    Bt, L, D = inp["x"].shape
+    N = inp["A"].shape[1]
+    y = torch.full((Bt, L, D), float("nan"), dtype=G.torch_dtype(idt), device="cuda")
+    hl = torch.full((Bt, D, N), float("nan"), device="cuda")
+    a = ssm.make_scan_args(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], h0d, hl, y,
+                           t["conv_w"] if conv else None, t["conv_b"] if conv else None, zoh,
+                           chunk_len)
+    return a, y, hl, (t, h0d)
+
+
+def _run_noalloc(a):
+    lib = ssm.load_library()
+    st = lib.ssm_scan_fwd_noalloc(ctypes.byref(a), torch.cuda.current_stream().cuda_stream)
+    assert st == 0, lib.ssm_last_error_message()
+
+
+def _run_plain(a):
+    lib = ssm.load_library()
+    need = int(lib.ssm_scan_workspace_size(ctypes.byref(a)))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    st = lib.ssm_scan_fwd(ctypes.byref(a), torch.cuda.current_stream().cuda_stream)
+    assert st == 0, lib.ssm_last_error_message()
+    torch.cuda.synchronize()
+    a.workspace, a.workspace_bytes = None, 0
+    return need
+
+
+# (batch, L, D, N, dtype, zoh, conv, h0): the second is smaller than the first
+CALLS = [(4, 3000, 300, 16, "f32", False, False, True),
+         (2, 1000, 130, 16, "bf16", True, True, True)]
+
+
+def test_noalloc_matches_scan_twice():
+    for i, (Bt, L, D, N, idt, zoh, conv, h0) in enumerate(CALLS):
+        w = SI.Workload("noalloc", 160 + i, Bt, L, D, N, idt, idt, zoh=zoh,
+                        conv_k=4 if conv else 0, a_dist="random", dskip_dist="uniform")
+        inp = SI.scan_inputs(w, seed=4000 + i, h0=h0)
+        G.say("noalloc call", i, (Bt, L, D, N, idt, zoh, conv))
+        a, y, hl, keep = _args(inp, idt, zoh, h0, conv=conv)
+        need = int(ssm.load_library().ssm_scan_workspace_size(ctypes.byref(a)))
+        assert 0 < need <= ssm.NOALLOC_SCRATCH_BYTES, need
+        _run_noalloc(a)
+        torch.cuda.synchronize()
+        y_na, h_na = y.clone(), hl.clone()
+        y.fill_(float("nan"))
+        hl.fill_(float("nan"))
+        _run_plain(a)
+        assert torch.equal(y_na, y), "y differs from ssm_scan_fwd (call %d)" % i
+        assert torch.equal(h_na, hl), "h_last differs from ssm_scan_fwd (call %d)" % i
+        y_ref, h_ref = G.oracle_scan(inp, zoh=zoh, h0=h0)
+        G.compare(G.host(y_na), y_ref, G.TOL[idt], "noalloc y call %d" % i)
+        G.compare(h_na.cpu().numpy(), h_ref, G.TOL[idt], "noalloc h_last call %d" % i)
+
+
+def test_noalloc_lengthens_chunks_to_fit():
+    """A problem whose ordinary plan keeps more summaries than the scratch
+    array holds (1 x 2^19 x 512 x 16, 2048 chunks, about 71 MB): the
+    allocation-free call takes longer chunks and matches the oracle; a
+    forced chunk length whose summaries do not fit is refused before any
+    launch, with the outputs untouched."""
+    Bt, L, D, N = 1, 1 << 19, 512, 16
+    w = SI.Workload("noallocbig", 170, Bt, L, D, N, "bf16", "bf16")
+    inp = SI.scan_inputs(w, seed=4100)
+    a, y, hl, keep = _args(inp, "bf16", False, False)
+    lib = ssm.load_library()
+    need = int(lib.ssm_scan_workspace_size(ctypes.byref(a)))
+    G.say("ordinary plan needs", need, "bytes")
+    assert need > ssm.NOALLOC_SCRATCH_BYTES
+    a.chunk_len = 64
+    st = lib.ssm_scan_fwd_noalloc(ctypes.byref(a), torch.cuda.current_stream().cuda_stream)
+    assert st == ssm.SSM_ERR_WORKSPACE, st
+    assert b"scratch" in lib.ssm_last_error_message()
+    torch.cuda.synchronize()
+    assert torch.isnan(y.float()).all() and torch.isnan(hl).all()
+    a.chunk_len = 0
+    _run_noalloc(a)
+    torch.cuda.synchronize()
+    yh, hh = G.host(y), hl.cpu().numpy()
+    for d0 in range(0, D, 64):
+        ds = slice(d0, d0 + 64)
+        y_ref, h_ref = G.oracle_scan(G.channel_slice(inp, 0, ds), h0=False)
+        G.compare(yh[:, :, ds], y_ref, G.TOL["bf16"], "noalloc long y channels %d.." % d0)
+        G.compare(hh[:, ds], h_ref, G.TOL["bf16"], "noalloc long h_last channels %d.." % d0)
