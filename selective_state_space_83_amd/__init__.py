@@ -125,6 +125,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError("%s is not built; run __graft_entry__.build() or "
                            "python -m selective_state_space_83_amd._build" % path)
+    # PyTorch first: the library then binds to the HIP runtime PyTorch loads
+    # (the same soname); loaded before it, the library would bring in the
+    # system runtime, and launches would not see the device PyTorch uses
+    _torch()
     lib = ctypes.CDLL(path)
     lib.ssm_abi_version.restype = ctypes.c_int
     lib.ssm_abi_version.argtypes = []
