@@ -107,9 +107,10 @@ __device__ __forceinline__ bool any_exact(const ChanConst<NS, DISC>& cc, float d
 // states before (hp) and after (hn) the step, form the gradient terms of the
 // step (pB, pC per state; du and dDelta summed over the lane's states, both
 // overwritten), add the step's dA terms and move the adjoint g to the
-// previous step.  `exact` (wave-uniform) carries the decay as
-// G + expm1(Delta A) G for slow decay; only that product differs between the
-// two forms, so the rest of the step is shared code.  SERIES (some state of
+// previous step.  `exact` (wave-uniform) adds to a G, for slow decay, the
+// part r G that rounding took from a (r = exp(Delta A) - a, see
+// exp_residual); only that product differs between the two forms, so the
+// rest of the step is shared code.  SERIES (some state of
 // the wave has |z| < 1/16) evaluates ZOH's factor f = expm1(z) / A and df/dA,
 // for the states with small |z| = |Delta A|, by their series:
 //   f = Delta (1 + z/2 + z^2/6 + z^3/24 + z^4/120),
@@ -132,11 +133,9 @@ __device__ __forceinline__ void bwd_lane_step(float (&g)[NS], float (&dA)[NS],
     G[n] = fmaf(Cv[n], dyv, g[n]);
   }
   if (exact) {
-    // (the expm1 form only where the decay is weak: G + expm1 G cancels for
-    // a strong one, see decay_add)
+    // a G plus what rounding took from a (see decay_add)
 #pragma unroll
-    for (int n = 0; n < NS; ++n)
-      ag[n] = (a[n] > 0.5f) ? fmaf(expm1_from(z2[n], a[n]), G[n], G[n]) : a[n] * G[n];
+    for (int n = 0; n < NS; ++n) ag[n] = fmaf(a[n], G[n], exp_residual<true>(z2[n], a[n]) * G[n]);
   } else {
 #pragma unroll
     for (int n = 0; n < NS; ++n) ag[n] = a[n] * G[n];
@@ -255,7 +254,7 @@ k_bwd_summary(const BwdParams p) {
         const float z2 = dv * cc.A2[n];
         const float G = fmaf(Ccur[n], dyv, g[n]);
         const float a = exp2_fast(z2);
-        g[n] = (a > 0.5f) ? fmaf(expm1_from(z2, a), G, G) : a * G;
+        g[n] = fmaf(a, G, exp_residual<true>(z2, a) * G);
       }
     } else {
 #pragma unroll
@@ -600,7 +599,7 @@ k_bwd_main(const BwdParams p) {
           }
           if (j < len) {
             if (any_exact<NS, DISC>(cc, da[jj]))
-              ssm_step_lane<NS, DISC, false, true>(h, cc, Bv, Bv, xa[jj], da[jj]);
+              ssm_step_lane<NS, DISC, false, true, true>(h, cc, Bv, Bv, xa[jj], da[jj]);
             else
               ssm_step_lane<NS, DISC, false, false>(h, cc, Bv, Bv, xa[jj], da[jj]);
           }

@@ -44,11 +44,11 @@
 // that rounding it to fp32 biases the decay rate by up to 2^-24 / |Delta A|,
 // and with a steady Delta that bias compounds over the whole memory horizon.
 // At any step where some lane has min_n |Delta A[n]| below a threshold, the
-// wave instead carries the decay as e = expm1(Delta A), evaluated by its
-// series for small arguments:  h' = h + e h + Bbar u.  That form is used only
-// where Abar > 1/2: for a strong decay h + e h cancels, leaving a rounding
-// error of the size of the old h rather than of Abar h, so there the decay is
-// applied directly (Abar h + Bbar u) -- in the same wave, per state.
+// wave adds back what rounding took from Abar: with r = exp(Delta A) - Abar,
+// from the expm1 series where |Delta A| < 1/16 and 0 elsewhere, it steps
+// h' = Abar h + (r h + Bbar u).  A strong decay thus stays the direct product
+// Abar h (no h + expm1 h that would cancel to a rounding error of the size of
+// the old h), with no per-state choice between two forms.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -235,22 +235,42 @@ __device__ __forceinline__ void load_chan(ChanConst<N, DISC>& cc, const float* A
   cc.thr = (amin > 0.0f) ? thr_scale / amin : __builtin_inff();
 }
 
-// expm1(z) given z2 = z * log2(e) and a = exp2(z2): the series
-// z (1 + z/2 + z^2/6 + z^3/24 + z^4/120) below |z| = 1/16 (truncation error
-// under 4e-11 relative), a - 1 above it (relative error under ~1e-6 there).
-__device__ __forceinline__ float expm1_from(float z2, float a) {
+// exp(z) - a given z2 = z * log2(e) and a = exp2(z2), the part of exp(z)
+// that rounding a to fp32 lost.  Below |z| = 1/16 it is (1 - a) + expm1(z),
+// with 1 - a exact (a lies within [1/2, 2]) and expm1 from its series
+// z (1 + z/2 + z^2/6 + z^3/24 + z^4/120) (truncation error under 4e-11
+// relative); above it, 0 (a is then within ~1e-6 of exp(z) relative to 1 - a).
+//
+// Two evaluations of the same value.  SELECT picks between the series and 0
+// with a compare.  The default takes the series at z clamped to
+// [-1/16, 1/16] and multiplies it by a factor that is exactly 1 for
+// |z| < 1/16 and exactly 0 otherwise: 2^40 (1/16 - |z|) clamped to [0, 1]
+// (fp32 values of |z| differ from 1/16 by 2^-28 or more, so the product is
+// never strictly between 0 and 1).  It needs no compare, hence no lane-mask
+// registers, which the unrolled steps otherwise hold one per state.  Which
+// compiles to faster code depends on the kernel around it (measured: the
+// clamped form in the forward passes, the select in the backward pass).
+template <bool SELECT = false>
+__device__ __forceinline__ float exp_residual(float z2, float a) {
   const float z = z2 * kLn2;
-  float p = fmaf(z, 1.0f / 120.0f, 1.0f / 24.0f);
-  p = fmaf(z, p, 1.0f / 6.0f);
-  p = fmaf(z, p, 0.5f);
-  p = fmaf(z, p, 1.0f);
-  return (fabsf(z) < 0.0625f) ? z * p : a - 1.0f;
+  const float zs = SELECT ? z : __builtin_amdgcn_fmed3f(z, -0.0625f, 0.0625f);
+  float p = fmaf(zs, 1.0f / 120.0f, 1.0f / 24.0f);
+  p = fmaf(zs, p, 1.0f / 6.0f);
+  p = fmaf(zs, p, 0.5f);
+  p = fmaf(zs, p, 1.0f);
+  if constexpr (SELECT) {
+    return (fabsf(z) < 0.0625f) ? fmaf(z, p, 1.0f - a) : 0.0f;
+  } else {
+    const float m = __builtin_amdgcn_fmed3f(fmaf(-fabsf(z), 0x1p40f, 0x1p36f), 0.0f, 1.0f);
+    return fmaf(zs, p, 1.0f - a) * m;
+  }
 }
 
 // One time step for one lane: updates h[] and returns sum_n C[n] h[n].
 // u is the scan input, dv = Delta.  WITH_Y = false skips the readout.
-// EXACT selects the slow-decay form (see the header).
-template <int N, int DISC, bool WITH_Y, bool EXACT>
+// EXACT selects the slow-decay form (see the header); SELECT the evaluation
+// of its residual (see exp_residual).
+template <int N, int DISC, bool WITH_Y, bool EXACT, bool SELECT = false>
 __device__ __forceinline__ float ssm_step_lane(float (&h)[N], const ChanConst<N, DISC>& cc,
                                                const float (&Bv)[N], const float (&Cv)[N],
                                                float u, float dv) {
@@ -268,14 +288,15 @@ __device__ __forceinline__ float ssm_step_lane(float (&h)[N], const ChanConst<N,
         h[n] = fmaf(a, h[n] + q, -q);
       }
     } else {
-      const float e = expm1_from(z2, a);
+      const float r = exp_residual<SELECT>(z2, a);
       float gu;   // the input factor times u
       if constexpr (DISC == kDeltaB) {
         gu = du;
       } else {
+        const float e = (a - 1.0f) + r;   // expm1(Delta A)
         gu = (cc.invA[n] != 0.0f) ? (e * cc.invA[n]) * u : du;   // A = 0: limit Delta
       }
-      h[n] = (a > 0.5f) ? fmaf(e, h[n], fmaf(gu, Bv[n], h[n])) : fmaf(a, h[n], gu * Bv[n]);
+      h[n] = fmaf(a, h[n], fmaf(gu, Bv[n], r * h[n]));
     }
     if constexpr (WITH_Y) {
       if (n & 1) acc1 = fmaf(Cv[n], h[n], acc1);
@@ -655,12 +676,10 @@ k_chunk_summary(const ScanParams p) {
 }
 
 // exp(z) * carry + b with z2 = z * log2(e), keeping the decay accurate when
-// exp(z) is close to 1 (carry + expm1(z) carry + b), and applied directly
-// when it is not (where carry + expm1(z) carry would cancel, leaving a
-// rounding error of the size of the carry itself).
+// exp(z) is close to 1: a carry + (r carry + b) with r = exp(z) - a.
 __device__ __forceinline__ float decay_add(float z2, float carry, float b) {
   const float a = exp2_fast(z2);
-  return (a > 0.5f) ? fmaf(expm1_from(z2, a), carry, carry + b) : fmaf(a, carry, b);
+  return fmaf(a, carry, fmaf(exp_residual(z2, a), carry, b));
 }
 
 // Exclusive walk over G groups: vals[g] (a group's end state from zero) is

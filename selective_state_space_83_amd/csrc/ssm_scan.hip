@@ -363,7 +363,8 @@ ssm_status_t check_step(const ssm_step_args_t* a) {
 }
 
 // A step where some lane has min_n |Delta A[n]| below this threshold runs
-// the slow-decay form (expm1 of Delta A) instead of the fast one.  The fast
+// the slow-decay form (Abar plus its rounding residual, from the expm1
+// series of Delta A) instead of the fast one.  The fast
 // form's error is about 2^-24 / |Delta A| relative: on the decay rate for
 // Delta*B, and additionally on the input term for ZOH ((a - 1) / A).  The
 // thresholds keep that well inside the tolerance of each input precision.

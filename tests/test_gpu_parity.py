@@ -391,6 +391,41 @@ def test_long_memory_lti_closed_form():
             G.compare(y[b, ts, d], ref, G.TOL["f32"], "longmem LTI b=%d d=%d cl=%d" % (b, d, cl))
 
 
+def test_lti_closed_form_zoh():
+    """The LTI closed form with the exact ZOH discretization: Delta, B, C drawn
+    once per batch row and held constant, so y_t = sum_j K_{t-j} x_j + D x_t
+    with K_k = sum_n C[n] (Abar[n] - 1) / A[n] B[n] Abar[n]^k, summed here in
+    fp64 over the whole history for sampled steps and channels, against the
+    GPU scan in its own plan and with a forced short chunk."""
+    w = SI.Workload("ltizoh", 14, 2, 8192, 128, 16, "f32", "f32", zoh=True, a_dist="random",
+                    dskip_dist="uniform")
+    inp = SI.scan_inputs(w, lti=True)
+    L = w.seqlen
+    rng = np.random.default_rng(10)
+    fixed = [0, 1, 2, 63, 64, L // 2, L - 1]
+    pool = np.setdiff1d(np.arange(3, L - 1), fixed)
+    ts = sorted(fixed + [int(t) for t in rng.choice(pool, 41, replace=False)])
+    chans = [0, 5, 63, 64, 100, 127]
+    k = np.arange(L, dtype=np.float64)
+    refs = {}
+    for b in range(w.batch):
+        Bv = inp["B"][b, 0].astype(np.float64)
+        Cv = inp["C"][b, 0].astype(np.float64)
+        for d in chans:
+            dt = float(inp["delta"][b, 0, d])
+            A = inp["A"][d].astype(np.float64)
+            abar = np.exp(dt * A)
+            f = np.expm1(dt * A) / A
+            K = (Cv * f * Bv * abar[None, :] ** k[:, None]).sum(axis=1)
+            x = inp["x"][b, :, d].astype(np.float64)
+            refs[b, d] = np.array([float(np.dot(K[:t + 1], x[t::-1])) + float(inp["D"][d]) * x[t]
+                                   for t in ts])
+    for cl in (0, 40):
+        y, _ = G.gpu_scan(inp, "f32", "f32", zoh=True, chunk_len=cl, h0=False, want_h_last=False)
+        for (b, d), ref in refs.items():
+            G.compare(y[b, ts, d], ref, G.TOL["f32"], "ZOH LTI b=%d d=%d cl=%d" % (b, d, cl))
+
+
 # ---------------------------------------------------------------------------
 # pins and invariants on the GPU
 # ---------------------------------------------------------------------------
