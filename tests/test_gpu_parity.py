@@ -603,7 +603,7 @@ def test_empty_sequence_hands_back_h0():
 
 def test_zoh_zero_A_and_tiny_delta():
     """ZOH limits: A = 0 gives Bbar = Delta B; tiny |Delta A| takes the
-    expm1-accurate branch.  Both dtypes."""
+    slow-decay branch (expm1 series).  Both dtypes."""
     for idt in ("f32", "bf16"):
         w = SI.Workload("z", 10, 2, 500, 96, 16, idt, "f32", zoh=True, a_dist="random")
         inp = SI.scan_inputs(w, seed=21, h0=True)
