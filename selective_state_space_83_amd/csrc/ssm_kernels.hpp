@@ -266,21 +266,48 @@ __device__ __forceinline__ float exp_residual(float z2, float a) {
   }
 }
 
+// The A a scaled ZOH state runs with: A itself, except that |A| below 2^-60
+// (A = 0 included) becomes -2^-60 (keeping a positive A's sign).  A h then
+// stays in fp32's normal range wherever h does, down to |h| ~ 2^-66, and
+// can be divided out again; the substitution changes exp(Delta A) by about
+// Delta 2^-60 and (exp(Delta A) - 1) / A, the input factor, by a relative
+// Delta 2^-61: far below fp32 resolution for any Delta a model uses.  (Such
+// a tiny |Delta A| always takes the slow-decay form, whose series keeps both
+// exact.)  The scaled state assumes |A h| stays below fp32's overflow limit.
+__device__ __forceinline__ float scaled_a(float A) {
+  return (A > 0.0f) ? fmaxf(A, 0x1p-60f) : fminf(A, -0x1p-60f);
+}
+
 // One time step for one lane: updates h[] and returns sum_n C[n] h[n].
 // u is the scan input, dv = Delta.  WITH_Y = false skips the readout.
 // EXACT selects the slow-decay form (see the header); SELECT the evaluation
 // of its residual (see exp_residual).
-template <int N, int DISC, bool WITH_Y, bool EXACT, bool SELECT = false>
+//
+// SCALED (ZOH without readout) carries g = A h in place of h.  With Bbar =
+// (Abar - 1) / A B the step becomes g' = Abar g + (Abar - 1) B u, evaluated
+// as Abar (g + B u) - B u: three operations per state where h takes four
+// (two products form (B u) / A).  The caller converts g back to h, and runs
+// it with A replaced by scaled_a(A).
+template <int N, int DISC, bool WITH_Y, bool EXACT, bool SELECT = false, bool SCALED = false>
 __device__ __forceinline__ float ssm_step_lane(float (&h)[N], const ChanConst<N, DISC>& cc,
                                                const float (&Bv)[N], const float (&Cv)[N],
                                                float u, float dv) {
+  static_assert(!SCALED || (DISC == kZoh && !WITH_Y), "the scaled state is ZOH's, without readout");
   float acc0 = 0.0f, acc1 = 0.0f;
   const float du = dv * u;
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     const float z2 = dv * cc.A2[n];
     const float a = exp2_fast(z2);
-    if constexpr (!EXACT) {
+    if constexpr (SCALED) {
+      const float bu = u * Bv[n];
+      if constexpr (!EXACT) {
+        h[n] = fmaf(a, h[n] + bu, -bu);
+      } else {
+        const float r = exp_residual<SELECT>(z2, a);
+        h[n] = fmaf(a, h[n], fmaf((a - 1.0f) + r, bu, r * h[n]));   // (a - 1) + r = expm1
+      }
+    } else if constexpr (!EXACT) {
       if constexpr (DISC == kDeltaB) {
         h[n] = fmaf(a, h[n], du * Bv[n]);
       } else {
@@ -306,14 +333,14 @@ __device__ __forceinline__ float ssm_step_lane(float (&h)[N], const ChanConst<N,
   return acc0 + acc1;
 }
 
-template <int N, int DISC, bool WITH_Y>
+template <int N, int DISC, bool WITH_Y, bool SCALED = false>
 __device__ __forceinline__ float ssm_step_any(float (&h)[N], const ChanConst<N, DISC>& cc,
                                               const float (&Bv)[N], const float (&Cv)[N],
                                               float u, float dv) {
   // wave-uniform choice: the fast form unless some lane has a tiny |Delta A|
   if (__builtin_amdgcn_ballot_w64(dv < cc.thr) != 0)
-    return ssm_step_lane<N, DISC, WITH_Y, true>(h, cc, Bv, Cv, u, dv);
-  return ssm_step_lane<N, DISC, WITH_Y, false>(h, cc, Bv, Cv, u, dv);
+    return ssm_step_lane<N, DISC, WITH_Y, true, false, SCALED>(h, cc, Bv, Cv, u, dv);
+  return ssm_step_lane<N, DISC, WITH_Y, false, false, SCALED>(h, cc, Bv, Cv, u, dv);
 }
 
 // Causal conv window: taps w[0..3] (oldest .. newest, zero-padded at the
@@ -453,20 +480,27 @@ __device__ __forceinline__ void stb(__amdgpu_buffer_rsrc_t r, uint32_t voff, uin
 // GATE (output pass only) streams z like x and multiplies each output by
 // silu(z).  SAVE (output pass only) writes the state entering every
 // kSaveStride-th step to p.hsave.  cs_save, when not null, receives the conv window after the last
-// step (the caller passes it for the final chunk only).
+// step (the caller passes it for the final chunk only).  SCALED (ZOH summary
+// pass, from a zero state) carries A h through the chunk (see ssm_step_lane)
+// and converts it back to h after the last step.
 template <int N, typename InT, typename OutT, int DISC, bool CONV, bool OUT, bool GATE,
-          bool SAVE = false>
+          bool SAVE = false, bool SCALED = false>
 __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64_t dbase,
                                            uint32_t lo, int64_t t0, int32_t steps, float (&h)[N],
                                            float* dsum_out, float* cs_save) {
   static_assert(OUT || !GATE, "the gate applies to the output pass");
   static_assert(OUT || !SAVE, "the output pass keeps the states");
+  static_assert(!SCALED || (!OUT && DISC == kZoh), "the scaled state is the ZOH summary's");
   // (the conv prologue's extra registers would push an 8-step summary block
   // past 128 VGPRs, so conv summaries prefetch 6 steps ahead)
   constexpr int kU = OUT ? kUnrollOut : (CONV ? 6 : kUnrollSum);
   const int64_t d = dbase + lo;
   ChanConst<N, DISC> cc;
   load_chan<N, DISC>(cc, p.A + d * N, p.exact_thr);
+  if constexpr (SCALED) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) cc.A2[n] = scaled_a(p.A[d * N + n]) * kLog2e;
+  }
   const float dsk = (OUT && p.Dskip) ? p.Dskip[d] : 0.0f;
   const int dtm = p.dt_mode;
   const float dtb = (dtm != kDtRaw && p.dt_bias) ? p.dt_bias[d] : 0.0f;
@@ -532,7 +566,7 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
       stb(ry, lo_out, soff_out, yv, static_cast<OutT*>(nullptr));
       soff_out += row_out;
     } else {
-      ssm_step_any<N, DISC, false>(h, cc, Bcur, Bcur, u, dv);
+      ssm_step_any<N, DISC, false, SCALED>(h, cc, Bcur, Bcur, u, dv);
     }
     Brow += N;
     Crow += N;
@@ -642,6 +676,12 @@ __device__ __forceinline__ void chunk_loop(const ScanParams& p, int64_t b, int64
     }
   }
   if (!OUT && dsum_out) *dsum_out = dacc - dcomp;
+  if constexpr (SCALED) {
+    // back to h (A is read again rather than kept in registers through the
+    // chunk)
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] /= scaled_a(p.A[d * N + n]);
+  }
   if constexpr (CONV && OUT) {
     if (cs_save) conv_save(cs, p.conv_k, cs_save);
   }
@@ -668,8 +708,9 @@ k_chunk_summary(const ScanParams p) {
 #pragma unroll
   for (int n = 0; n < N; ++n) h[n] = 0.0f;
   const int64_t slot = tl.b * (p.C - 1) + tl.chunk;
-  chunk_loop<N, InT, float, DISC, CONV, false, false>(p, tl.b, dbase, lo, t0, steps, h,
-                                                      p.dsum + slot * p.D + d, nullptr);
+  // (ZOH carries the scaled state A h, see ssm_step_lane)
+  chunk_loop<N, InT, float, DISC, CONV, false, false, false, DISC == kZoh>(
+      p, tl.b, dbase, lo, t0, steps, h, p.dsum + slot * p.D + d, nullptr);
   float* hs = p.hsum + (slot * p.D + d) * N;
 #pragma unroll
   for (int n = 0; n < N; ++n) hs[n] = h[n];
