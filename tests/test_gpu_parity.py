@@ -601,6 +601,30 @@ def test_empty_sequence_hands_back_h0():
     assert torch.count_nonzero(hl) == 0
 
 
+@pytest.mark.parametrize("conv", [False, True])
+def test_zoh_summary_extreme_A(conv):
+    """The ZOH summary pass carries A h with |A| below 2^-60 run as
+    -2^-60 (sign kept for positive A).  Channels whose states mix A = 0,
+    tiny A of both signs (one subnormal), growing A > 0 and a strong decay
+    (A = -500) must still match the oracle through several chunks."""
+    for idt in ("f32", "bf16"):
+        w = SI.Workload("za", 11, 2, 300, 128, 16, idt, "f32", zoh=True, a_dist="random",
+                        conv_k=4 if conv else 0)
+        inp = SI.scan_inputs(w, seed=23, h0=True)
+        A = inp["A"]
+        A[3, :] = 0.0
+        A[10, 0], A[10, 1], A[10, 2], A[10, 3] = 1e-25, -1e-25, -3e-39, 0.0
+        A[20, 5] = 0.5
+        A[21, :] = 0.25
+        A[30, 9] = -500.0
+        A[64 + 7, 2] = 2e-30          # a second wave of channels
+        A[64 + 7, 15] = -500.0
+        y, hl = G.gpu_scan(inp, idt, "f32", zoh=True, h0=True, chunk_len=32)
+        y_ref, h_ref = G.oracle_scan(inp, zoh=True, h0=True)
+        G.compare(y, y_ref, G.TOL[idt], "zoh extreme A y %s conv=%s" % (idt, conv))
+        G.compare(hl, h_ref, G.TOL[idt], "zoh extreme A h %s conv=%s" % (idt, conv))
+
+
 def test_zoh_zero_A_and_tiny_delta():
     """ZOH limits: A = 0 gives Bbar = Delta B; tiny |Delta A| takes the
     slow-decay branch (expm1 series).  Both dtypes."""
