@@ -75,6 +75,7 @@ struct BwdParams {
   int32_t dtiles;
   int32_t nwg;
   float exact_thr;
+  float series_z;        // ZOH: |Delta A| below this takes f and df/dA from their series
 };
 
 template <int N>
@@ -110,13 +111,19 @@ __device__ __forceinline__ bool any_exact(const ChanConst<NS, DISC>& cc, float d
 // previous step.  `exact` (wave-uniform) adds to a G, for slow decay, the
 // part r G that rounding took from a (r = exp(Delta A) - a, see
 // exp_residual); only that product differs between the two forms, so the
-// rest of the step is shared code.  SERIES (some state of
-// the wave has |z| < 1/16) evaluates ZOH's factor f = expm1(z) / A and df/dA,
-// for the states with small |z| = |Delta A|, by their series:
+// rest of the step is shared code.  SERIES (some state of the wave has |z|
+// below series_z) evaluates ZOH's factor f = expm1(z) / A and df/dA, for the
+// states with |z| = |Delta A| below series_z, by their series:
 //   f = Delta (1 + z/2 + z^2/6 + z^3/24 + z^4/120),
 //   df/dA = Delta^2 (1/2 + z/3 + z^2/8 + z^3/30 + z^4/144),
-// which also give the A = 0 limits; (a - 1) / A and (Delta a - f) / A lose
-// relative precision there.
+// which also give the A = 0 limits.  The direct forms (a - 1) / A and
+// (Delta a - f) / A carry the rounding of a (about 2^-24) divided by the
+// difference they take: relative errors of about 2^-24 / |z| in f and
+// 2^-23 / z^2 in df/dA (up to twice that with the exp's own rounding; an
+// fp32 emulation over random A and Delta at |z| just above the threshold
+// found at most 5.8e-5 at 1/16 and 7.8e-4 at 1/64).  series_z is set per
+// input precision so that this stays far inside the tolerance: 1/16 for
+// fp32 inputs, 1/64 for bf16.  (The truncated series holds for |z| < 1/16.)
 template <int NS, int DISC, bool SERIES>
 __device__ __forceinline__ void bwd_lane_step(float (&g)[NS], float (&dA)[NS],
                                               const ChanConst<NS, DISC>& cc,
@@ -124,7 +131,7 @@ __device__ __forceinline__ void bwd_lane_step(float (&g)[NS], float (&dA)[NS],
                                               const float (&hp)[NS], const float (&hn)[NS],
                                               float u, float dv, float dyv, bool exact,
                                               float (&pB)[NS], float (&pC)[NS], float& du,
-                                              float& ddt) {
+                                              float& ddt, float series_z) {
   float z2[NS], a[NS], G[NS], ag[NS];
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
@@ -177,7 +184,7 @@ __device__ __forceinline__ void bwd_lane_step(float (&g)[NS], float (&dA)[NS],
         q2 = fmaf(z, q2, 0.125f);
         q2 = fmaf(z, q2, 1.0f / 3.0f);
         q2 = fmaf(z, q2, 0.5f);
-        const bool small = fabsf(z) < 0.0625f || cc.invA[n] == 0.0f;
+        const bool small = fabsf(z) < series_z || cc.invA[n] == 0.0f;
         f = small ? dv * q1 : f;
         dfda = small ? (dv * dv) * q2 : dfda;
       }
@@ -449,13 +456,13 @@ k_bwd_main(const BwdParams p) {
   load_chan<NS, DISC>(cc, p.A + d * N + n0, p.exact_thr);
   const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
   // ZOH's factor is taken from its series when some |Delta A[n]| of the wave
-  // is below 1/16 (where (a - 1) / A would lose relative precision)
+  // is below p.series_z (see bwd_lane_step)
   float zoh_thr = 0.0f;
   if constexpr (DISC == kZoh) {
     float amin = __builtin_inff();
 #pragma unroll
     for (int n = 0; n < NS; ++n) amin = fminf(amin, fabsf(cc.A2[n] * kLn2));
-    zoh_thr = amin > 0.0f ? 0.0625f / amin : __builtin_inff();
+    zoh_thr = amin > 0.0f ? p.series_z / amin : __builtin_inff();
   }
 
   // adjoint entering the end of this super-chunk
@@ -671,10 +678,10 @@ k_bwd_main(const BwdParams p) {
           const bool series = DISC == kZoh && __builtin_amdgcn_ballot_w64(dv < zoh_thr) != 0;
           if (series)
             bwd_lane_step<NS, DISC, true>(g, dAacc, cc, Bv, Cv, stash[js], hn, u, dv, dyv,
-                                          exact, pB, pC, du, ddt);
+                                          exact, pB, pC, du, ddt, p.series_z);
           else
             bwd_lane_step<NS, DISC, false>(g, dAacc, cc, Bv, Cv, stash[js], hn, u, dv, dyv,
-                                           exact, pB, pC, du, ddt);
+                                           exact, pB, pC, du, ddt, p.series_z);
           dDacc = fmaf(dyv, u, dDacc);   // every wave sums it; wave 0 stores it
         }
         const int sp = jj & 1;   // the pair (jj | 1, jj & ~1) shares the rows
