@@ -75,7 +75,6 @@ struct BwdParams {
   int32_t dtiles;
   int32_t nwg;
   float exact_thr;
-  float series_z;        // ZOH: |Delta A| below this takes f and df/dA from their series
 };
 
 template <int N>
@@ -121,17 +120,22 @@ __device__ __forceinline__ bool any_exact(const ChanConst<NS, DISC>& cc, float d
 // difference they take: relative errors of about 2^-24 / |z| in f and
 // 2^-23 / z^2 in df/dA (up to twice that with the exp's own rounding; an
 // fp32 emulation over random A and Delta at |z| just above the threshold
-// found at most 5.8e-5 at 1/16 and 7.8e-4 at 1/64).  series_z is set per
-// input precision so that this stays far inside the tolerance: 1/16 for
-// fp32 inputs, 1/64 for bf16.  (The truncated series holds for |z| < 1/16.)
-template <int NS, int DISC, bool SERIES>
+// found at most 5.8e-5 at 1/16 and 7.8e-4 at 1/64).  The threshold is set
+// per input precision so that this stays far inside the tolerance (see
+// series_z): 1/16 for fp32 inputs, 1/64 for bf16 (SHORT), where the series
+// are cut after their z^2 terms (truncation under 2.5e-7 relative below
+// |z| = 1/64; the five-term series hold for |z| < 1/16).
+template <bool SHORT>
+constexpr float series_z() { return SHORT ? 1.0f / 64.0f : 1.0f / 16.0f; }
+
+template <int NS, int DISC, bool SERIES, bool SHORT>
 __device__ __forceinline__ void bwd_lane_step(float (&g)[NS], float (&dA)[NS],
                                               const ChanConst<NS, DISC>& cc,
                                               const float (&Bv)[NS], const float (&Cv)[NS],
                                               const float (&hp)[NS], const float (&hn)[NS],
                                               float u, float dv, float dyv, bool exact,
                                               float (&pB)[NS], float (&pC)[NS], float& du,
-                                              float& ddt, float series_z) {
+                                              float& ddt) {
   float z2[NS], a[NS], G[NS], ag[NS];
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
@@ -176,15 +180,21 @@ __device__ __forceinline__ void bwd_lane_step(float (&g)[NS], float (&dA)[NS],
         // some state of the wave has |z| < 1/16: the series there, the direct
         // forms elsewhere (the series is truncated for small |z| only)
         const float z = z2[n] * kLn2;
-        float q1 = fmaf(z, 1.0f / 120.0f, 1.0f / 24.0f);
-        q1 = fmaf(z, q1, 1.0f / 6.0f);
-        q1 = fmaf(z, q1, 0.5f);
-        q1 = fmaf(z, q1, 1.0f);
-        float q2 = fmaf(z, 1.0f / 144.0f, 1.0f / 30.0f);
-        q2 = fmaf(z, q2, 0.125f);
-        q2 = fmaf(z, q2, 1.0f / 3.0f);
-        q2 = fmaf(z, q2, 0.5f);
-        const bool small = fabsf(z) < series_z || cc.invA[n] == 0.0f;
+        float q1, q2;
+        if constexpr (SHORT) {
+          q1 = fmaf(z, fmaf(z, 1.0f / 6.0f, 0.5f), 1.0f);
+          q2 = fmaf(z, fmaf(z, 0.125f, 1.0f / 3.0f), 0.5f);
+        } else {
+          q1 = fmaf(z, 1.0f / 120.0f, 1.0f / 24.0f);
+          q1 = fmaf(z, q1, 1.0f / 6.0f);
+          q1 = fmaf(z, q1, 0.5f);
+          q1 = fmaf(z, q1, 1.0f);
+          q2 = fmaf(z, 1.0f / 144.0f, 1.0f / 30.0f);
+          q2 = fmaf(z, q2, 0.125f);
+          q2 = fmaf(z, q2, 1.0f / 3.0f);
+          q2 = fmaf(z, q2, 0.5f);
+        }
+        const bool small = fabsf(z) < series_z<SHORT>() || cc.invA[n] == 0.0f;
         f = small ? dv * q1 : f;
         dfda = small ? (dv * dv) * q2 : dfda;
       }
@@ -456,13 +466,14 @@ k_bwd_main(const BwdParams p) {
   load_chan<NS, DISC>(cc, p.A + d * N + n0, p.exact_thr);
   const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
   // ZOH's factor is taken from its series when some |Delta A[n]| of the wave
-  // is below p.series_z (see bwd_lane_step)
+  // is below series_z (see bwd_lane_step)
+  constexpr bool kShortSeries = !std::is_same<InT, float>::value;
   float zoh_thr = 0.0f;
   if constexpr (DISC == kZoh) {
     float amin = __builtin_inff();
 #pragma unroll
     for (int n = 0; n < NS; ++n) amin = fminf(amin, fabsf(cc.A2[n] * kLn2));
-    zoh_thr = amin > 0.0f ? p.series_z / amin : __builtin_inff();
+    zoh_thr = amin > 0.0f ? series_z<kShortSeries>() / amin : __builtin_inff();
   }
 
   // adjoint entering the end of this super-chunk
@@ -677,11 +688,11 @@ k_bwd_main(const BwdParams p) {
           const bool exact = any_exact<NS, DISC>(cc, dv);
           const bool series = DISC == kZoh && __builtin_amdgcn_ballot_w64(dv < zoh_thr) != 0;
           if (series)
-            bwd_lane_step<NS, DISC, true>(g, dAacc, cc, Bv, Cv, stash[js], hn, u, dv, dyv,
-                                          exact, pB, pC, du, ddt, p.series_z);
+            bwd_lane_step<NS, DISC, true, kShortSeries>(g, dAacc, cc, Bv, Cv, stash[js], hn, u,
+                                                        dv, dyv, exact, pB, pC, du, ddt);
           else
-            bwd_lane_step<NS, DISC, false>(g, dAacc, cc, Bv, Cv, stash[js], hn, u, dv, dyv,
-                                           exact, pB, pC, du, ddt, p.series_z);
+            bwd_lane_step<NS, DISC, false, kShortSeries>(g, dAacc, cc, Bv, Cv, stash[js], hn, u,
+                                                         dv, dyv, exact, pB, pC, du, ddt);
           dDacc = fmaf(dyv, u, dDacc);   // every wave sums it; wave 0 stores it
         }
         const int sp = jj & 1;   // the pair (jj | 1, jj & ~1) shares the rows

@@ -749,9 +749,6 @@ ssm_status_t run_bwd(const ssm_scan_bwd_args_t* a, const BwdPlan& pl, hipStream_
   bp.Cf = pl.Cf;
   bp.dtiles = int32_t(pl.dtiles);
   bp.exact_thr = thr;
-  // below this |Delta A| the ZOH backward takes f and df/dA from their series
-  // (the direct forms' relative error in df/dA is about 2^-23 / |Delta A|^2)
-  bp.series_z = a->in_dtype == SSM_BF16 ? 1.0f / 64.0f : 1.0f / 16.0f;
   if (pl.Cs > 1) {
     bp.nwg = int32_t(a->batch * (pl.Cs - 1) * pl.dtiles);
     hipLaunchKernelGGL((k_bwd_summary<N, InT, DISC>), dim3(bp.nwg), dim3(kWave), 0, s, bp);
