@@ -200,8 +200,9 @@ __device__ __forceinline__ void bwd_lane_step(float (&g)[NS], float (&dA)[NS],
       }
       const float agh = ag[n] * hp[n];
       const float Bu = Bv[n] * u;
-      pB[n] = G[n] * (f * u);
-      su = fmaf(G[n] * f, Bv[n], su);
+      const float Gf = G[n] * f;
+      pB[n] = Gf * u;
+      su = fmaf(Gf, Bv[n], su);
       dt2 = fmaf(cc.A2[n], agh, dt2);
       dtb = fmaf(ag[n], Bu, dtb);                        // df/dDelta = a
       dA[n] = fmaf(dv, agh, fmaf(G[n] * dfda, Bu, dA[n]));
