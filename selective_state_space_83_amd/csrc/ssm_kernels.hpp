@@ -960,6 +960,124 @@ __device__ __forceinline__ void store_state(float* p, const float (&h)[NL]) {
   }
 }
 
+// Single pass with one lane per state: a channel's N states sit on N
+// consecutive lanes (kWave / N channels per wave), every step is computed
+// once, and the readout sum over the states crosses lanes by DPP.  It has no
+// chunk summaries and no carry walk: one launch walks the whole sequence.
+// Each wave has kWave / N channels instead of kWave, so it suits problems
+// with few sequences and channels, where the chunked plan's waves would
+// stay few and short and its three launches dominate (the plan picks it).
+// The per-(b, t, d) work (Delta u, the step-size transform, the skip term)
+// repeats on every lane of a channel, and B and C are per-lane loads.
+// No conv prologue (the plan routes conv to the chunked passes); GATE
+// multiplies y by silu(z); SAVE writes the state entering every
+// kSaveStride-th step to p.hsave.
+template <int N>
+__device__ __forceinline__ float lanes_sum(float v) {
+  if constexpr (N >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  if constexpr (N >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  // row_half_mirror, row_mirror: lane i meets lane 7 - i, then 15 - i
+  if constexpr (N >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  if constexpr (N >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+template <int N, typename InT, typename OutT, int DISC, bool GATE, bool SAVE>
+__global__ void __launch_bounds__(kWave) k_scan_split(const ScanParams p) {
+  constexpr int CPW = kWave / N;   // channels per wave
+  constexpr int K = 8;             // steps per prefetched block
+  const int wg = xcd_remap(blockIdx.x, p.nwg);
+  const int64_t ctiles = (p.D + CPW - 1) / CPW;
+  const int64_t b = wg / ctiles;
+  const int64_t D = p.D, L = p.L;
+  const int lane = threadIdx.x;
+  const int n = lane % N;
+  int64_t d = (wg - b * ctiles) * CPW + lane / N;
+  if (d > D - 1) d = D - 1;   // lanes past the last channel repeat channel D - 1
+  ChanConst<1, DISC> cc;
+  load_chan<1, DISC>(cc, p.A + d * N + n, p.exact_thr);
+  const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
+  const int dtm = p.dt_mode;
+  const float dtb = (dtm != kDtRaw && p.dt_bias) ? p.dt_bias[d] : 0.0f;
+  float h[1] = {p.h0 ? p.h0[(b * D + d) * N + n] : 0.0f};
+  // rows of x, Delta, z (and y) are D elements, rows of B and C N elements;
+  // the plan keeps L * D * 4 bytes below 2^31
+  const int64_t xo = b * L * D, bo = b * L * N;
+  const uint32_t row = static_cast<uint32_t>(D * sizeof(InT));
+  const uint32_t rowo = static_cast<uint32_t>(D * sizeof(OutT));
+  const uint32_t rown = static_cast<uint32_t>(N * sizeof(InT));
+  const uint32_t lx = static_cast<uint32_t>(d * sizeof(InT)), ly = static_cast<uint32_t>(d * sizeof(OutT));
+  const uint32_t ln = static_cast<uint32_t>(n * sizeof(InT));
+  const uint32_t span = static_cast<uint32_t>(L) * row;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const InT*>(p.x) + xo, span);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(static_cast<const InT*>(p.delta) + xo, span);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(static_cast<const InT*>(GATE ? p.z : p.x) + xo, GATE ? span : 0u);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(static_cast<const InT*>(p.Bm) + bo, static_cast<uint32_t>(L) * rown);
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(static_cast<const InT*>(p.Cm) + bo, static_cast<uint32_t>(L) * rown);
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<OutT*>(p.y) + xo, static_cast<uint32_t>(L) * rowo);
+  constexpr InT* kIn = nullptr;
+  constexpr OutT* kOut = nullptr;
+  float* save_dst = SAVE ? p.hsave + (b * p.nsave * D + d) * N + n : nullptr;
+  // block loads, rows clamped to the last (loaded but unused past L)
+  float xc[K], dc[K], bc[K], ccv[K], zc[K];
+  auto load_block = [&](int64_t t0, float (&xs)[K], float (&ds)[K], float (&bs)[K], float (&cs)[K],
+                        float (&zs)[K]) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t t = (t0 + j < L) ? t0 + j : L - 1;
+      xs[j] = ldb(rx, lx, static_cast<uint32_t>(t) * row, kIn);
+      ds[j] = ldb(rd, lx, static_cast<uint32_t>(t) * row, kIn);
+      bs[j] = ldb(rb, ln, static_cast<uint32_t>(t) * rown, kIn);
+      cs[j] = ldb(rc, ln, static_cast<uint32_t>(t) * rown, kIn);
+      zs[j] = GATE ? ldb(rz, lx, static_cast<uint32_t>(t) * row, kIn) : 0.0f;
+    }
+  };
+  load_block(0, xc, dc, bc, ccv, zc);
+  for (int64_t t0 = 0; t0 < L; t0 += K) {
+    float xn[K], dn[K], bn[K], cn[K], zn[K];
+    load_block(t0 + K, xn, dn, bn, cn, zn);
+    if (dtm != kDtRaw) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) dc[j] = dt_transform(dc[j], dtb, dtm);
+    }
+    // One wave-uniform choice of the step form per block (the slow-decay
+    // form for the whole block if any lane needs it at any of its steps),
+    // so that a full block is straight-line code whose steps overlap.  The
+    // channel's lanes all hold the reduced sum and store the same y.
+    auto run_block = [&](auto form) {
+      constexpr int F = decltype(form)::value;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int64_t t = t0 + j;
+        if (t >= L) break;   // wave-uniform
+        if constexpr (SAVE) {
+          if (t > 0 && t % kSaveStride == 0) save_dst[(t / kSaveStride - 1) * D * N] = h[0];
+        }
+        const float Bv[1] = {bc[j]}, Cv[1] = {ccv[j]};
+        const float acc =
+            lanes_sum<N>(ssm_step_lane<1, DISC, true, F == 1>(h, cc, Bv, Cv, xc[j], dc[j]));
+        float yv = fmaf(dsk, xc[j], acc);
+        if constexpr (GATE) yv *= silu(zc[j]);
+        stb(ry, ly, static_cast<uint32_t>(t) * rowo, yv, kOut);
+      }
+    };
+    float dmin = dc[0];
+#pragma unroll
+    for (int j = 1; j < K; ++j) dmin = fminf(dmin, dc[j]);
+    if (__builtin_amdgcn_ballot_w64(dmin < cc.thr) != 0) run_block(std::integral_constant<int, 1>{});
+    else run_block(std::integral_constant<int, 0>{});
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      xc[j] = xn[j];
+      dc[j] = dn[j];
+      bc[j] = bn[j];
+      ccv[j] = cn[j];
+      zc[j] = zn[j];
+    }
+  }
+  if (p.h_last) p.h_last[(b * D + d) * N + n] = h[0];
+}
+
 // One decode step per sequence, h updated in place.  A wave covers CPW
 // channels of ROWS consecutive batch rows (a row past the batch is skipped,
 // uniformly for the wave).  Lanes past the last channel duplicate channel

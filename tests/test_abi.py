@@ -450,12 +450,33 @@ def test_plan_and_workspace(lib, shape):
     ((4, 2048, 768, 16), 32),        # four per SIMD would cut 28-step chunks: three per SIMD
     ((8, 4096, 384, 16), 64),        # 52 -> 64
     ((8, 1024, 512, 16), 24),        # 16 -> 24
-    ((2, 64, 32, 16), 8),            # the minimum chunk binds
+    ((2, 64, 32, 16), 64),           # short, few channels: one pass, a lane per state
+    ((2, 128, 32, 16), 8),           # too long for one pass: the minimum chunk binds
     ((256, 4096, 5120, 16), 4096),   # enough waves without cutting the sequence
 ])
 def test_auto_plan(lib, shape, T):
     b, L, D, N = shape
     assert plan(lib, batch=b, L=L, D=D, N=N)[0] == T
+
+
+def test_single_pass_plan_rule(lib):
+    """Short sequences of few channels (seqlen <= 64, at most 1024 waves of
+    one lane per state) take the single pass: the plan reports seqlen and
+    needs no workspace.  A forced chunk length, a conv prologue, a longer
+    sequence or more waves keep the chunked passes."""
+    assert plan(lib, batch=2, L=64, D=128, N=16) == (64, 0)           # 64 waves
+    assert plan(lib, batch=4, L=64, D=1024, N=16) == (64, 0)          # 1024 waves
+    assert plan(lib, batch=1, L=1, D=1, N=1) == (1, 0)
+    T, ws = plan(lib, batch=5, L=64, D=1024, N=16)                    # 1280 waves
+    assert T < 64 and ws > 0
+    T, ws = plan(lib, batch=2, L=65, D=128, N=16)
+    assert T < 65 and ws > 0
+    T, ws = plan(lib, batch=2, L=64, D=128, N=16, chunk_len=8)
+    assert T == 8 and ws > 0
+    a = valid_scan_args(batch=2, L=64, D=128, N=16)
+    a.conv_w, a.conv_k = 0x100000000 + 12 * GB, 4
+    assert lib.ssm_scan_plan_chunk_len(ctypes.byref(a)) < 64
+    assert lib.ssm_scan_workspace_size(ctypes.byref(a)) > 0
 
 
 def test_plan_respects_chunk_len(lib):
