@@ -960,122 +960,162 @@ __device__ __forceinline__ void store_state(float* p, const float (&h)[NL]) {
   }
 }
 
-// Single pass with one lane per state: a channel's N states sit on N
-// consecutive lanes (kWave / N channels per wave), every step is computed
-// once, and the readout sum over the states crosses lanes by DPP.  It has no
-// chunk summaries and no carry walk: one launch walks the whole sequence.
-// Each wave has kWave / N channels instead of kWave, so it suits problems
-// with few sequences and channels, where the chunked plan's waves would
-// stay few and short and its three launches dominate (the plan picks it).
-// The per-(b, t, d) work (Delta u, the step-size transform, the skip term)
-// repeats on every lane of a channel, and B and C are per-lane loads.
-// No conv prologue (the plan routes conv to the chunked passes); GATE
-// multiplies y by silu(z); SAVE writes the state entering every
-// kSaveStride-th step to p.hsave.
-template <int N>
-__device__ __forceinline__ float lanes_sum(float v) {
-  if constexpr (N >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-  if constexpr (N >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-  // row_half_mirror, row_mirror: lane i meets lane 7 - i, then 15 - i
-  if constexpr (N >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
-  if constexpr (N >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
-  return v;
+// Time across the lanes: one wave per channel (b, d), lane i holding step
+// t0 + i of a block of 64 steps.  Every lane forms its step's pair
+// (Abar, Bbar u) for each state at once, and an inclusive scan over the
+// lanes by the associative operator (a, b) o (a', b') = (a a', a' b + b')
+// (53ai.com explainer, section 3.3; gsyq.cn deep-dive, 硬件优化并行扫描算法:
+// the recurrence evaluated as a tree) leaves in lane i the state that the
+// block's steps up to t0 + i reach from a zero state, and the decay product
+// over them.  The scan takes six DPP steps across the wave: row_shr 1, 2,
+// 4, 8 within each row of 16 lanes, then row_bcast 15 and row_bcast 31
+// across rows; a lane whose DPP source lies outside its reach keeps the
+// identity (1, 0).  The block's carry-in h then enters as A_i h + b_i, and
+// lane 63's state carries into the next block.  A block costs one dependent
+// chain of six combines instead of 64 dependent steps, so a short sequence
+// of few channels finishes in a fraction of a sequential walk's latency;
+// each element costs about six combines of work instead of one step, so the
+// plan takes it only for short sequences of few channels, where the chunked
+// passes' three launches and their waves' first-step latencies dominate.
+//
+// Weak decays.  Where some step of the block has |Delta A| below the
+// slow-decay threshold (wave-uniform test), each decay is carried as a pair
+// a + r, with r the part of exp(Delta A) that rounding a lost
+// (exp_residual), and the product of two decays keeps its own rounding
+// error, fma(a, a', -a a'), in r.  No conv prologue (the plan routes conv to
+// the chunked passes); GATE multiplies y by silu(z); SAVE writes the state
+// entering every kSaveStride-th step to p.hsave.
+// One combine of the lane scan: every lane takes the pair of the lane CTRL
+// reaches (the identity where it reaches none) as the earlier operand.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_from(float v, float id) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(id), __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+
+template <int CTRL, int ROWS, bool RES, int N>
+__device__ __forceinline__ void wave_combine(float (&a)[N], float (&r)[N], float (&bb)[N]) {
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const float ap = dpp_from<CTRL, ROWS>(a[n], 1.0f);
+    const float bp = dpp_from<CTRL, ROWS>(bb[n], 0.0f);
+    if constexpr (RES) {
+      const float rp = dpp_from<CTRL, ROWS>(r[n], 0.0f);
+      // (ap + rp, bp) o (a + r, b): b' = (a + r) bp + b, decay (ap + rp)(a + r)
+      // with the rounding error of ap a kept in r (rp r is below fp32 resolution)
+      bb[n] = fmaf(a[n], bp, fmaf(r[n], bp, bb[n]));
+      const float m = ap * a[n];
+      r[n] = fmaf(ap, a[n], -m) + fmaf(ap, r[n], rp * a[n]);
+      a[n] = m;
+    } else {
+      bb[n] = fmaf(a[n], bp, bb[n]);
+      a[n] = ap * a[n];
+    }
+  }
+}
+
+// Inclusive scan of the pairs over the 64 lanes: row_shr 1, 2, 4, 8 within
+// each row of 16 lanes, then row_bcast 15 into rows 1 and 3 and row_bcast 31
+// into rows 2 and 3.
+template <bool RES, int N>
+__device__ __forceinline__ void wave_scan(float (&a)[N], float (&r)[N], float (&bb)[N]) {
+  wave_combine<0x111, 0xF, RES>(a, r, bb);
+  wave_combine<0x112, 0xF, RES>(a, r, bb);
+  wave_combine<0x114, 0xF, RES>(a, r, bb);
+  wave_combine<0x118, 0xF, RES>(a, r, bb);
+  wave_combine<0x142, 0xA, RES>(a, r, bb);
+  wave_combine<0x143, 0xC, RES>(a, r, bb);
 }
 
 template <int N, typename InT, typename OutT, int DISC, bool GATE, bool SAVE>
-__global__ void __launch_bounds__(kWave) k_scan_split(const ScanParams p) {
-  constexpr int CPW = kWave / N;   // channels per wave
-  constexpr int K = 8;             // steps per prefetched block
-  const int wg = xcd_remap(blockIdx.x, p.nwg);
-  const int64_t ctiles = (p.D + CPW - 1) / CPW;
-  const int64_t b = wg / ctiles;
+__global__ void __launch_bounds__(kWave) k_scan_wave(const ScanParams p) {
+  const int64_t wg = blockIdx.x;
   const int64_t D = p.D, L = p.L;
+  const int64_t b = wg / D, d = wg - b * D;
   const int lane = threadIdx.x;
-  const int n = lane % N;
-  int64_t d = (wg - b * ctiles) * CPW + lane / N;
-  if (d > D - 1) d = D - 1;   // lanes past the last channel repeat channel D - 1
-  ChanConst<1, DISC> cc;
-  load_chan<1, DISC>(cc, p.A + d * N + n, p.exact_thr);
+  ChanConst<N, DISC> cc;
+  load_chan<N, DISC>(cc, p.A + d * N, p.exact_thr);
   const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
   const int dtm = p.dt_mode;
   const float dtb = (dtm != kDtRaw && p.dt_bias) ? p.dt_bias[d] : 0.0f;
-  float h[1] = {p.h0 ? p.h0[(b * D + d) * N + n] : 0.0f};
-  // rows of x, Delta, z (and y) are D elements, rows of B and C N elements;
-  // the plan keeps L * D * 4 bytes below 2^31
-  const int64_t xo = b * L * D, bo = b * L * N;
-  const uint32_t row = static_cast<uint32_t>(D * sizeof(InT));
-  const uint32_t rowo = static_cast<uint32_t>(D * sizeof(OutT));
-  const uint32_t rown = static_cast<uint32_t>(N * sizeof(InT));
-  const uint32_t lx = static_cast<uint32_t>(d * sizeof(InT)), ly = static_cast<uint32_t>(d * sizeof(OutT));
-  const uint32_t ln = static_cast<uint32_t>(n * sizeof(InT));
-  const uint32_t span = static_cast<uint32_t>(L) * row;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const InT*>(p.x) + xo, span);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(static_cast<const InT*>(p.delta) + xo, span);
-  const __amdgpu_buffer_rsrc_t rz = make_rsrc(static_cast<const InT*>(GATE ? p.z : p.x) + xo, GATE ? span : 0u);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(static_cast<const InT*>(p.Bm) + bo, static_cast<uint32_t>(L) * rown);
-  const __amdgpu_buffer_rsrc_t rc = make_rsrc(static_cast<const InT*>(p.Cm) + bo, static_cast<uint32_t>(L) * rown);
-  const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<OutT*>(p.y) + xo, static_cast<uint32_t>(L) * rowo);
-  constexpr InT* kIn = nullptr;
-  constexpr OutT* kOut = nullptr;
-  float* save_dst = SAVE ? p.hsave + (b * p.nsave * D + d) * N + n : nullptr;
-  // block loads, rows clamped to the last (loaded but unused past L)
-  float xc[K], dc[K], bc[K], ccv[K], zc[K];
-  auto load_block = [&](int64_t t0, float (&xs)[K], float (&ds)[K], float (&bs)[K], float (&cs)[K],
-                        float (&zs)[K]) {
+  const InT* xp = static_cast<const InT*>(p.x) + b * L * D + d;
+  const InT* dp = static_cast<const InT*>(p.delta) + b * L * D + d;
+  const InT* zp = static_cast<const InT*>(GATE ? p.z : p.x) + b * L * D + d;
+  const InT* Bp = static_cast<const InT*>(p.Bm) + b * L * N;
+  const InT* Cp = static_cast<const InT*>(p.Cm) + b * L * N;
+  OutT* yp = static_cast<OutT*>(p.y) + b * L * D + d;
+  float hc[N];   // state entering the block (wave-uniform)
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const int64_t t = (t0 + j < L) ? t0 + j : L - 1;
-      xs[j] = ldb(rx, lx, static_cast<uint32_t>(t) * row, kIn);
-      ds[j] = ldb(rd, lx, static_cast<uint32_t>(t) * row, kIn);
-      bs[j] = ldb(rb, ln, static_cast<uint32_t>(t) * rown, kIn);
-      cs[j] = ldb(rc, ln, static_cast<uint32_t>(t) * rown, kIn);
-      zs[j] = GATE ? ldb(rz, lx, static_cast<uint32_t>(t) * row, kIn) : 0.0f;
+  for (int n = 0; n < N; ++n) hc[n] = p.h0 ? p.h0[(b * D + d) * N + n] : 0.0f;
+  for (int64_t t0 = 0; t0 < L; t0 += kWave) {
+    const int64_t t = t0 + lane;
+    const bool in = t < L;
+    const int64_t tc = in ? t : L - 1;   // lanes past the end read the last step
+    float u = ld(xp + tc * D);
+    float dv = ld(dp + tc * D);
+    if (dtm != kDtRaw) dv = dt_transform(dv, dtb, dtm);
+    const float zv = GATE ? ld(zp + tc * D) : 0.0f;
+    if (!in) {   // the identity pair: a = exp(0) = 1, b = 0
+      u = 0.0f;
+      dv = 0.0f;
     }
-  };
-  load_block(0, xc, dc, bc, ccv, zc);
-  for (int64_t t0 = 0; t0 < L; t0 += K) {
-    float xn[K], dn[K], bn[K], cn[K], zn[K];
-    load_block(t0 + K, xn, dn, bn, cn, zn);
-    if (dtm != kDtRaw) {
+    float Bv[N], Cv[N];
 #pragma unroll
-      for (int j = 0; j < K; ++j) dc[j] = dt_transform(dc[j], dtb, dtm);
+    for (int n = 0; n < N; ++n) {
+      Bv[n] = ld(Bp + tc * N + n);
+      Cv[n] = ld(Cp + tc * N + n);
     }
-    // One wave-uniform choice of the step form per block (the slow-decay
-    // form for the whole block if any lane needs it at any of its steps),
-    // so that a full block is straight-line code whose steps overlap.  The
-    // channel's lanes all hold the reduced sum and store the same y.
-    auto run_block = [&](auto form) {
-      constexpr int F = decltype(form)::value;
+    float h[N];
+    // the block's pairs, scanned; RES carries each decay's rounding residual
+    auto block = [&](auto form) {
+      constexpr bool RES = decltype(form)::value;
+      float a[N], r[N], bb[N];
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
-        const int64_t t = t0 + j;
-        if (t >= L) break;   // wave-uniform
-        if constexpr (SAVE) {
-          if (t > 0 && t % kSaveStride == 0) save_dst[(t / kSaveStride - 1) * D * N] = h[0];
+      for (int n = 0; n < N; ++n) {
+        const float z2 = dv * cc.A2[n];
+        a[n] = exp2_fast(z2);
+        r[n] = (RES || DISC == kZoh) ? exp_residual<true>(z2, a[n]) : 0.0f;
+        float gu;   // the input factor times u
+        if constexpr (DISC == kDeltaB) {
+          gu = dv * u;
+        } else {
+          const float e = (a[n] - 1.0f) + r[n];   // expm1(Delta A)
+          gu = (cc.invA[n] != 0.0f) ? (e * cc.invA[n]) * u : dv * u;   // A = 0: limit Delta
         }
-        const float Bv[1] = {bc[j]}, Cv[1] = {ccv[j]};
-        const float acc =
-            lanes_sum<N>(ssm_step_lane<1, DISC, true, F == 1>(h, cc, Bv, Cv, xc[j], dc[j]));
-        float yv = fmaf(dsk, xc[j], acc);
-        if constexpr (GATE) yv *= silu(zc[j]);
-        stb(ry, ly, static_cast<uint32_t>(t) * rowo, yv, kOut);
+        bb[n] = gu * Bv[n];
       }
+      wave_scan<RES>(a, r, bb);
+#pragma unroll
+      for (int n = 0; n < N; ++n)
+        h[n] = RES ? fmaf(a[n], hc[n], fmaf(r[n], hc[n], bb[n])) : fmaf(a[n], hc[n], bb[n]);
     };
-    float dmin = dc[0];
+    if (__builtin_amdgcn_ballot_w64(dv < cc.thr) != 0) block(std::true_type{});
+    else block(std::false_type{});
+    float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
-    for (int j = 1; j < K; ++j) dmin = fminf(dmin, dc[j]);
-    if (__builtin_amdgcn_ballot_w64(dmin < cc.thr) != 0) run_block(std::integral_constant<int, 1>{});
-    else run_block(std::integral_constant<int, 0>{});
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      xc[j] = xn[j];
-      dc[j] = dn[j];
-      bc[j] = bn[j];
-      ccv[j] = cn[j];
-      zc[j] = zn[j];
+    for (int n = 0; n < N; ++n) {
+      if (n & 1) acc1 = fmaf(Cv[n], h[n], acc1);
+      else acc0 = fmaf(Cv[n], h[n], acc0);
     }
+    float yv = fmaf(dsk, u, acc0 + acc1);
+    if constexpr (GATE) yv *= silu(zv);
+    if (in) st(yp + t * D, yv);
+    if constexpr (SAVE) {
+      // lane t holds the state entering step t + 1
+      if (in && t + 1 < L && (t + 1) % kSaveStride == 0) {
+        float* dst = p.hsave + ((b * p.nsave + (t + 1) / kSaveStride - 1) * D + d) * N;
+#pragma unroll
+        for (int n = 0; n < N; ++n) dst[n] = h[n];
+      }
+    }
+    if (p.h_last && t == L - 1) {
+#pragma unroll
+      for (int n = 0; n < N; ++n) p.h_last[(b * D + d) * N + n] = h[n];
+    }
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+      hc[n] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h[n]), kWave - 1));
   }
-  if (p.h_last) p.h_last[(b * D + d) * N + n] = h[0];
 }
 
 // One decode step per sequence, h updated in place.  A wave covers CPW

@@ -113,7 +113,7 @@ Grouping grouping(int64_t nc, int64_t chains) {
 }
 
 struct Plan {
-  bool split = false;  // single pass, one lane per state (k_scan_split); C = 1
+  bool wave = false;   // one pass, lanes over time steps, a DPP scan per block (k_scan_wave); C = 1
   int64_t T = 0;       // chunk length
   int64_t C = 0;       // chunks
   int64_t dtiles = 0;  // ceil(D / 64)
@@ -159,31 +159,34 @@ Plan make_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t chunk_len) {
   return pl;
 }
 
-// Whether a problem takes the single-pass lane-split kernel: no conv
-// prologue (the chunked passes carry its window), no forced chunk length,
-// 32-bit buffer offsets, and a shape where it measured faster than the
-// chunked passes.  Its waves walk the whole sequence at about 0.14 us per
-// step when alone on a SIMD, so it wins only where the chunked plan's three
-// launches dominate: short sequences of few channels.  Measured (us per
-// call, chunked / split): 2 x 32 x 128 x 16 fp32 16.4 / 6.5; 1 x 64 x 32 x
-// 16 16.6 / 11.2; 2 x 64 x 32 x 16 14.9 / 10.7; but 1 x 128 x 256 x 16 bf16
-// 14.9 / 19.3, 16 x 64 x 2560 x 16 bf16 (10,240 waves) 37.1 / 55.4, and
-// 8 x 2048 x 1536 x 16 fp32 0.163 / 0.563 ms.
-constexpr int64_t kSplitMaxSteps = 64;
-constexpr int64_t kSplitMaxWaves = 1024;
-bool split_wins(int64_t Bt, int64_t L, int64_t D, int64_t N) {
-  const int64_t waves = Bt * ((D * N + ssmk::kWave - 1) / ssmk::kWave);
-  return L <= kSplitMaxSteps && waves <= kSplitMaxWaves;
+// Whether a problem takes the one-pass lane scan (k_scan_wave: time steps
+// across a wave's lanes, one wave per channel, a DPP scan per block of 64
+// steps): no conv prologue (the chunked passes carry its window), no forced
+// chunk length, and a short sequence of few channels.  A block's six
+// dependent combines take about 1.5 us alone on a SIMD, and every element
+// costs about six combines of work instead of one recurrence step, so it
+// wins where the chunked plan's three launches and its waves' first-step
+// latencies dominate: at most 8 blocks (seqlen <= 512) and at most 4096
+// wave-blocks (batch * dim * ceil(seqlen / 64)).  Measured, us per call
+// back to back (chunked or the earlier lane-split single pass / lane scan):
+// 2 x 64 x 32 x 16 fp32 10.3 / 6.2; 1 x 128 x 256 x 16 bf16 14.8 / 6.0;
+// 4 x 64 x 1024 x 16 fp32 12.4 / 9.6; 1 x 512 x 32 x 16 fp32 17.8 / 14.7;
+// 4 x 128 x 256 x 16 bf16 ZOH 17.2 / 8.5; but 1 x 1024 x 32 x 16 fp32
+// 19.6 / 27.2, 8 x 128 x 1024 x 16 fp32 ZOH 39.6 / 44.9 and
+// 16 x 64 x 2560 x 16 bf16 36.1 / 56.4.
+constexpr int64_t kWaveMaxSteps = 512;
+constexpr int64_t kWaveMaxBlocks = 4096;
+bool wave_wins(int64_t Bt, int64_t L, int64_t D) {
+  const int64_t blocks = (L + ssmk::kWave - 1) / ssmk::kWave;
+  return L <= kWaveMaxSteps && Bt * D <= kWaveMaxBlocks / blocks;
 }
 
-Plan split_plan(const ssm_scan_args_t* a, const Plan& chunked) {
-  const int64_t L = a->seqlen, D = a->dim, N = a->dstate;
+Plan one_pass_plan(const ssm_scan_args_t* a, const Plan& chunked) {
+  const int64_t L = a->seqlen, D = a->dim;
   if (a->conv_w || a->chunk_len > 0 || L == 0 || a->batch * D == 0) return chunked;
-  if (L * D * 4 > kMaxChunkBytes || L * N * 4 > kMaxChunkBytes) return chunked;
-  if (a->batch * ((D * N + ssmk::kWave - 1) / ssmk::kWave) > kMaxGrid) return chunked;
-  if (!split_wins(a->batch, L, D, N)) return chunked;
+  if (!wave_wins(a->batch, L, D)) return chunked;
   Plan pl;
-  pl.split = true;
+  pl.wave = true;
   pl.T = L;
   pl.C = 1;
   pl.dtiles = chunked.dtiles;
@@ -256,7 +259,7 @@ ssm_status_t check_scan(const ssm_scan_args_t* a, Plan* plan, bool own_scratch =
       !mul_ok(a->batch, dn, &bdn) || bld > INT64_MAX / 8 || bln > INT64_MAX / 8 ||
       bdn > INT64_MAX / 8 || !mul_ok(a->batch * a->dim, win, &bds) || bds > INT64_MAX / 8)
     return fail(SSM_ERR_SHAPE, "sizes overflow");
-  *plan = split_plan(a, own_scratch
+  *plan = one_pass_plan(a, own_scratch
                            ? scratch_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len)
                            : make_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len));
   if (own_scratch && plan->ws_total > kNoallocScratchBytes)
@@ -471,17 +474,16 @@ template <int N, typename InT, typename OutT, int DISC, bool CONV, bool GATE>
 ssm_status_t run_scan(ssmk::ScanParams kp, const Plan& pl, hipStream_t s, hipEvent_t ev0,
                       hipEvent_t ev1) {
   if constexpr (!CONV) {
-    if (pl.split) {
-      constexpr int64_t cpw = ssmk::kWave / N;
-      kp.nwg = int32_t(kp.Bt * ((kp.D + cpw - 1) / cpw));
+    if (pl.wave) {
+      kp.nwg = int32_t(kp.Bt * kp.D);
       if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return fail(SSM_ERR_HIP, "hipEventRecord failed");
       if (kp.hsave)
-        hipLaunchKernelGGL((ssmk::k_scan_split<N, InT, OutT, DISC, GATE, true>), dim3(kp.nwg),
+        hipLaunchKernelGGL((ssmk::k_scan_wave<N, InT, OutT, DISC, GATE, true>), dim3(kp.nwg),
                            dim3(ssmk::kWave), 0, s, kp);
       else
-        hipLaunchKernelGGL((ssmk::k_scan_split<N, InT, OutT, DISC, GATE, false>), dim3(kp.nwg),
+        hipLaunchKernelGGL((ssmk::k_scan_wave<N, InT, OutT, DISC, GATE, false>), dim3(kp.nwg),
                            dim3(ssmk::kWave), 0, s, kp);
-      if (ssm_status_t st = launch_status("k_scan_split")) return st;
+      if (ssm_status_t st = launch_status("k_scan_wave")) return st;
       if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return fail(SSM_ERR_HIP, "hipEventRecord failed");
       return SSM_OK;
     }
@@ -860,7 +862,7 @@ size_t ssm_scan_workspace_size(const ssm_scan_args_t* a) {
   if (!mul_ok(a->batch, a->seqlen, &bl) || !mul_ok(bl, a->dim, &bld) ||
       !mul_ok(a->batch, a->dim * a->dstate, &bdn))
     return 0;
-  return split_plan(a, make_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len)).ws_total;
+  return one_pass_plan(a, make_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len)).ws_total;
 }
 
 int64_t ssm_scan_plan_chunk_len(const ssm_scan_args_t* a) {
@@ -868,7 +870,7 @@ int64_t ssm_scan_plan_chunk_len(const ssm_scan_args_t* a) {
     return 0;
   int64_t bl, bld;
   if (!mul_ok(a->batch, a->seqlen, &bl) || !mul_ok(bl, a->dim, &bld)) return 0;
-  return split_plan(a, make_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len)).T;
+  return one_pass_plan(a, make_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len)).T;
 }
 
 }  // extern "C"

@@ -450,8 +450,9 @@ def test_plan_and_workspace(lib, shape):
     ((4, 2048, 768, 16), 32),        # four per SIMD would cut 28-step chunks: three per SIMD
     ((8, 4096, 384, 16), 64),        # 52 -> 64
     ((8, 1024, 512, 16), 24),        # 16 -> 24
-    ((2, 64, 32, 16), 64),           # short, few channels: one pass, a lane per state
-    ((2, 128, 32, 16), 8),           # too long for one pass: the minimum chunk binds
+    ((2, 64, 32, 16), 64),           # short, few channels: one pass, lanes over time
+    ((2, 128, 32, 16), 128),         # two blocks of 64 steps: still one pass
+    ((2, 1024, 32, 16), 8),          # too long for one pass: the minimum chunk binds
     ((256, 4096, 5120, 16), 4096),   # enough waves without cutting the sequence
 ])
 def test_auto_plan(lib, shape, T):
@@ -460,16 +461,21 @@ def test_auto_plan(lib, shape, T):
 
 
 def test_single_pass_plan_rule(lib):
-    """Short sequences of few channels (seqlen <= 64, at most 1024 waves of
-    one lane per state) take the single pass: the plan reports seqlen and
-    needs no workspace.  A forced chunk length, a conv prologue, a longer
-    sequence or more waves keep the chunked passes."""
-    assert plan(lib, batch=2, L=64, D=128, N=16) == (64, 0)           # 64 waves
-    assert plan(lib, batch=4, L=64, D=1024, N=16) == (64, 0)          # 1024 waves
+    """Short sequences of few channels (seqlen <= 512 and batch * dim *
+    ceil(seqlen / 64) <= 4096 blocks of 64 steps) take the one-pass lane
+    scan: the plan reports seqlen and needs no workspace.  A forced chunk
+    length, a conv prologue, a longer sequence or more channels keep the
+    chunked passes."""
+    assert plan(lib, batch=2, L=64, D=32, N=16) == (64, 0)            # 64 blocks
+    assert plan(lib, batch=4, L=64, D=1024, N=16) == (64, 0)          # 4096 blocks
+    assert plan(lib, batch=1, L=512, D=512, N=16) == (512, 0)         # 8 x 512
+    assert plan(lib, batch=2, L=65, D=1024, N=1) == (65, 0)           # 2 x 2 x 1024
     assert plan(lib, batch=1, L=1, D=1, N=1) == (1, 0)
-    T, ws = plan(lib, batch=5, L=64, D=1024, N=16)                    # 1280 waves
+    T, ws = plan(lib, batch=5, L=64, D=1024, N=16)                    # 5120 blocks
     assert T < 64 and ws > 0
-    T, ws = plan(lib, batch=2, L=65, D=128, N=16)
+    T, ws = plan(lib, batch=1, L=513, D=32, N=16)                     # past 512 steps
+    assert T < 513 and ws > 0
+    T, ws = plan(lib, batch=3, L=65, D=1024, N=16)                    # 6144 blocks
     assert T < 65 and ws > 0
     T, ws = plan(lib, batch=2, L=64, D=128, N=16, chunk_len=8)
     assert T == 8 and ws > 0

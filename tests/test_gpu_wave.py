@@ -1,10 +1,11 @@
-"""The single-pass plan (one lane per state, the readout summed across a
-channel's lanes), which the library takes for short sequences of few
-channels: every N, dtype pair and discretization, the fused step-size
-transforms and the gate, h0 or not, ragged channel counts and lengths below
-one prefetch block, steps whose tiny |Delta A| take the slow-decay form, and
-the states kept for the backward -- each compared element by element with the
-oracle.  The plan's choice itself is checked on the host in test_abi.py."""
+"""The one-pass plan for short sequences of few channels (time steps across
+a wave's lanes, each block of 64 steps solved by a scan over the lanes):
+every N, dtype pair and discretization, the fused step-size transforms and
+the gate, h0 or not, ragged channel counts, lengths within one block and
+across several (the carry from block to block), steps whose tiny |Delta A|
+make the scan carry each decay's rounding residual, and the states kept for
+the backward -- each compared element by element with the oracle.  The
+plan's choice itself is checked on the host in test_abi.py."""
 from __future__ import annotations
 
 import ctypes
@@ -45,7 +46,7 @@ for i, N in enumerate((1, 2, 4, 8, 16)):
         for zoh in (False, True):
             for use in ((), ("softplus", "gate"), ("bias",)):
                 k = len(CASES)
-                L = (1, 7, 17, 64)[k % 4]
+                L = (1, 7, 17, 64, 65, 200, 511)[k % 7]
                 D = (3, 65, 32, 130)[(k // 4) % 4]
                 Bt = 1 + k % 3
                 CASES.append((Bt, L, D, N, idt, odt, zoh, bool(k % 2), use))
@@ -69,15 +70,16 @@ def test_single_pass(case):
 
 @pytest.mark.parametrize("zoh", [False, True])
 def test_single_pass_slow_decay_and_kept_states(zoh):
-    """Tiny step sizes over part of the sequence (the slow-decay form, chosen
-    per block of steps), A = 0 in one channel, and the states kept every 16
-    steps for the backward, against the oracle's prefix scans."""
+    """Tiny step sizes over part of the sequence, across a block boundary (the
+    blocks holding them carry the decays' rounding residuals), A = 0 in one
+    channel, and the states kept every 16 steps for the backward, against the
+    oracle's prefix scans."""
     for idt in ("f32", "bf16"):
-        Bt, L, D, N = 2, 64, 40, 16
+        Bt, L, D, N = 2, 200, 40, 16
         w = SI.Workload("split_sd", 790, Bt, L, D, N, idt, idt, zoh=zoh, a_dist="random")
         inp = SI.scan_inputs(w, seed=31, h0=True)
         inp["A"][4, :] = 0.0
-        inp["delta"][:, 10:30, :] = SI._store(np.full((Bt, 20, D), 1e-6, np.float32), idt)
+        inp["delta"][:, 50:90, :] = SI._store(np.full((Bt, 40, D), 1e-6, np.float32), idt)
         assert _takes_single_pass(inp, idt, idt, zoh)
         t = {k: G.dev(inp[k], idt) for k in ("x", "delta", "B", "C")}
         A, Dv, h0 = G.dev(inp["A"]), G.dev(inp["D"]), G.dev(inp["h0"])
@@ -88,8 +90,8 @@ def test_single_pass_slow_decay_and_kept_states(zoh):
         G.compare(G.host(y), y_ref, G.TOL[idt], "y " + idt)
         G.compare(hl.cpu().numpy(), h_ref, G.TOL[idt], "h_last " + idt)
         kept = hs.cpu().numpy()
-        assert kept.shape == (Bt, 3, D, N)
-        for k, te in enumerate((16, 32, 48)):
+        assert kept.shape == (Bt, 12, D, N)
+        for k, te in enumerate(range(16, 200, 16)):
             sub = {key: (np.ascontiguousarray(v[:, :te]) if key in ("x", "delta", "B", "C") else v)
                    for key, v in inp.items()}
             _, h_te = G.oracle_scan(sub, zoh=zoh, h0=True)
