@@ -19,8 +19,8 @@ tiny, fp32 (8 x 2048 x 1536 x 16 fp32), conv (4 x 8192 x 2560 x 16 bf16 with
 the conv prologue and exact ZOH) and decode (512 consecutive ssm_step calls
 on 256 x 5120 x 16 timed as one step).
 
-Roofline of the dominant kernel (the output pass k_scan_out): its duration is
-measured per launch with HIP events that the library records around that
+Roofline of the dominant kernel (the output pass k_scan_out, or k_scan_wave
+where the plan is the one-pass lane scan): its duration is measured per launch with HIP events that the library records around that
 kernel on the launch stream.  Two roofs are evaluated:
   hbm  algorithmic bytes of the call / duration vs 8000 GB/s;
   alu  algorithmic VALU lane-slots / duration vs 256 CU x 4 SIMD x 16 lanes
@@ -242,6 +242,7 @@ def bench_scan(w, steps, warmup, torch, ssm, chunk_len=0, fused=False):
                                   chunk_len=chunk_len, **kw)
     ws_bytes = ssm.workspace_size(prep.args)
     chunk = ssm.plan_chunk_len(prep.args)
+    lane_scan = ssm.plan_lane_scan(prep.args)
     hip = HipEvents()
     evs = hip.create(4 * steps)       # the output pass of every timed step, both loops
     stream = torch.cuda.current_stream()
@@ -284,7 +285,8 @@ def bench_scan(w, steps, warmup, torch, ssm, chunk_len=0, fused=False):
     del flush
     return dict(inp=inp, flushed_ms=flushed_ms, wall_s=wall, out_ms=out_ms,
                 warm_ms=warm_total_ms / steps, out_ms_warm=out_ms_warm,
-                chunk_len=chunk, chunks=-(-w.seqlen // chunk), workspace=ws_bytes)
+                chunk_len=chunk, chunks=-(-w.seqlen // chunk), workspace=ws_bytes,
+                kernel="k_scan_wave" if lane_scan else "k_scan_out")
 
 
 def bench_decode(w, steps, warmup, torch, ssm, fused=False):
@@ -648,14 +650,14 @@ def main():
     alu_ach = slots / (out_us * 1e-6) / 1e12
     hbm_frac = hbm_ach / HBM_PEAK_GBS
     alu_frac = alu_ach / (SLOT_PEAK / 1e12)
-    traffic = None if args.fused else traffic_record(w.name)
+    traffic = None if args.fused else traffic_record(w.name, r["kernel"])
     if alu_frac > hbm_frac:
         roof = {"bound": "alu", "achieved": alu_ach, "peak": SLOT_PEAK / 1e12,
                 "unit": "T lane-slot/s", "frac": alu_frac, "traffic": traffic}
     else:
         roof = {"bound": "hbm", "achieved": hbm_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": hbm_frac, "traffic": traffic}
-    roof["kernel"] = "k_scan_out"
+    roof["kernel"] = r["kernel"]
     roof["kernel_us"] = out_us
     roof["kernel_us_warm"] = out_us_warm
     copy = copy_bandwidth(torch)

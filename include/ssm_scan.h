@@ -255,6 +255,12 @@ size_t ssm_scan_workspace_size(const ssm_scan_args_t* args);
  * section 3.3); that plan reports seqlen and needs no workspace. */
 int64_t ssm_scan_plan_chunk_len(const ssm_scan_args_t* args);
 
+/* 1 when the plan for these arguments is that one-pass lane scan (one
+ * kernel, k_scan_wave), 0 when it is the chunked passes (chunk summaries,
+ * carry combine and output pass; a single chunk runs the output pass alone)
+ * or the sizes are invalid.  Pure host function, no HIP call. */
+int32_t ssm_scan_plan_lane_scan(const ssm_scan_args_t* args);
+
 /* Selective-scan forward: y and (optionally) h_last from the inputs above.
  * The time axis may be split into chunks scanned in parallel; their carries
  * are combined with the associative operator

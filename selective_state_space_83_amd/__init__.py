@@ -108,6 +108,7 @@ class BwdArgs(ctypes.Structure):
 
 
 EXPORTS = ["ssm_abi_version", "ssm_scan_workspace_size", "ssm_scan_plan_chunk_len",
+           "ssm_scan_plan_lane_scan",
            "ssm_scan_fwd", "ssm_scan_fwd_noalloc", "ssm_step", "ssm_scan_bwd_workspace_size",
            "ssm_scan_bwd", "ssm_status_string", "ssm_last_error_message"]
 
@@ -136,6 +137,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanArgs)]
     lib.ssm_scan_plan_chunk_len.restype = ctypes.c_int64
     lib.ssm_scan_plan_chunk_len.argtypes = [ctypes.POINTER(ScanArgs)]
+    lib.ssm_scan_plan_lane_scan.restype = ctypes.c_int32
+    lib.ssm_scan_plan_lane_scan.argtypes = [ctypes.POINTER(ScanArgs)]
     lib.ssm_scan_fwd.restype = ctypes.c_int
     lib.ssm_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), ctypes.c_void_p]
     lib.ssm_scan_fwd_noalloc.restype = ctypes.c_int
@@ -321,6 +324,12 @@ def workspace_size(args: ScanArgs) -> int:
 
 def plan_chunk_len(args: ScanArgs) -> int:
     return int(load_library().ssm_scan_plan_chunk_len(ctypes.byref(args)))
+
+
+def plan_lane_scan(args: ScanArgs) -> bool:
+    """Whether the call runs the one-pass lane scan (k_scan_wave) rather than
+    the chunked passes."""
+    return bool(load_library().ssm_scan_plan_lane_scan(ctypes.byref(args)))
 
 
 def abi_version() -> int:

@@ -873,6 +873,14 @@ int64_t ssm_scan_plan_chunk_len(const ssm_scan_args_t* a) {
   return one_pass_plan(a, make_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len)).T;
 }
 
+int32_t ssm_scan_plan_lane_scan(const ssm_scan_args_t* a) {
+  if (!a || a->batch < 0 || a->seqlen < 0 || a->dim < 0 || a->dstate < 1 || a->chunk_len < 0)
+    return 0;
+  int64_t bl, bld;
+  if (!mul_ok(a->batch, a->seqlen, &bl) || !mul_ok(bl, a->dim, &bld)) return 0;
+  return one_pass_plan(a, make_plan(a->batch, a->seqlen, a->dim, a->dstate, a->chunk_len)).wave ? 1 : 0;
+}
+
 }  // extern "C"
 
 namespace {

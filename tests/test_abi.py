@@ -485,6 +485,33 @@ def test_single_pass_plan_rule(lib):
     assert lib.ssm_scan_workspace_size(ctypes.byref(a)) > 0
 
 
+def lane_scan(lib, **kw):
+    a = valid_scan_args(**kw)
+    return lib.ssm_scan_plan_lane_scan(ctypes.byref(a))
+
+
+def test_lane_scan_query(lib):
+    """ssm_scan_plan_lane_scan tells the one-pass lane scan from the chunked
+    passes, also where both report seqlen and no workspace (a chunked plan of
+    one chunk), and reads 0 for a conv prologue, a forced chunk length and
+    invalid sizes."""
+    assert lane_scan(lib, batch=2, L=64, D=32, N=16) == 1
+    assert lane_scan(lib, batch=1, L=512, D=512, N=16) == 1
+    assert lane_scan(lib, batch=5, L=64, D=1024, N=16) == 0
+    assert lane_scan(lib, batch=1, L=513, D=32, N=16) == 0
+    assert lane_scan(lib, batch=2, L=64, D=128, N=16, chunk_len=8) == 0
+    # one chunk of the chunked plan: same chunk length and workspace as the lane scan
+    assert plan(lib, batch=256, L=4, D=5120, N=16) == (4, 0)
+    assert lane_scan(lib, batch=256, L=4, D=5120, N=16) == 0
+    a = valid_scan_args(batch=2, L=64, D=128, N=16)
+    a.conv_w, a.conv_k = 0x100000000 + 12 * GB, 4
+    assert lib.ssm_scan_plan_lane_scan(ctypes.byref(a)) == 0
+    a = valid_scan_args(batch=2, L=64, D=32, N=16)
+    a.dstate = 0
+    assert lib.ssm_scan_plan_lane_scan(ctypes.byref(a)) == 0
+    assert lib.ssm_scan_plan_lane_scan(None) == 0
+
+
 def test_plan_respects_chunk_len(lib):
     for cl in (1, 7, 64, 100, 5000):
         T, ws = plan(lib, batch=2, L=1000, D=64, N=16, chunk_len=cl)

@@ -127,6 +127,7 @@ def test_library_host_code_under_sanitizers():
                 a.batch, a.seqlen, a.dim, a.dstate, a.chunk_len = b, L, D, N, cl
                 lib.ssm_scan_workspace_size(ctypes.byref(a))
                 lib.ssm_scan_plan_chunk_len(ctypes.byref(a))
+                lib.ssm_scan_plan_lane_scan(ctypes.byref(a))
                 g = ssm.BwdArgs()
                 g.batch, g.seqlen, g.dim, g.dstate = b, L, D, N
                 lib.ssm_scan_bwd_workspace_size(ctypes.byref(g))
