@@ -112,3 +112,32 @@ def test_noalloc_lengthens_chunks_to_fit():
         y_ref, h_ref = G.oracle_scan(G.channel_slice(inp, 0, ds), h0=False)
         G.compare(yh[:, :, ds], y_ref, G.TOL["bf16"], "noalloc long y channels %d.." % d0)
         G.compare(hh[:, ds], h_ref, G.TOL["bf16"], "noalloc long h_last channels %d.." % d0)
+
+
+def test_noalloc_lane_scan_plan():
+    """A short sequence of few channels (2 x 200 x 40 x 16), which both entry
+    points run as the one-pass lane scan with no scratch at all: the
+    allocation-free call equals ssm_scan_fwd bit for bit and the oracle at
+    the input precision's tolerance, whatever the scratch array holds from
+    earlier calls."""
+    for idt, zoh in (("f32", False), ("bf16", True)):
+        Bt, L, D, N = 2, 200, 40, 16
+        w = SI.Workload("noallocwave", 180, Bt, L, D, N, idt, idt, zoh=zoh, a_dist="random",
+                        dskip_dist="uniform")
+        inp = SI.scan_inputs(w, seed=4200, h0=True)
+        G.say("noalloc lane scan", (Bt, L, D, N, idt, zoh))
+        a, y, hl, keep = _args(inp, idt, zoh, True)
+        lib = ssm.load_library()
+        assert lib.ssm_scan_plan_lane_scan(ctypes.byref(a)) == 1
+        assert int(lib.ssm_scan_workspace_size(ctypes.byref(a))) == 0
+        _run_noalloc(a)
+        torch.cuda.synchronize()
+        y_na, h_na = y.clone(), hl.clone()
+        y.fill_(float("nan"))
+        hl.fill_(float("nan"))
+        _run_plain(a)
+        assert torch.equal(y_na, y), "y differs from ssm_scan_fwd"
+        assert torch.equal(h_na, hl), "h_last differs from ssm_scan_fwd"
+        y_ref, h_ref = G.oracle_scan(inp, zoh=zoh, h0=True)
+        G.compare(G.host(y_na), y_ref, G.TOL[idt], "noalloc lane scan y " + idt)
+        G.compare(h_na.cpu().numpy(), h_ref, G.TOL[idt], "noalloc lane scan h_last " + idt)
