@@ -168,8 +168,8 @@ Plan make_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t chunk_len) {
 // wins where the chunked plan's three launches and its waves' first-step
 // latencies dominate: at most 8 blocks (seqlen <= 512) and at most 4096
 // wave-blocks (batch * dim * ceil(seqlen / 64)).  Measured, us per call
-// back to back (chunked or the earlier lane-split single pass / lane scan):
-// 2 x 64 x 32 x 16 fp32 10.3 / 6.2; 1 x 128 x 256 x 16 bf16 14.8 / 6.0;
+// back to back (chunked passes / lane scan): 1 x 128 x 256 x 16 bf16
+// 14.8 / 6.0; 2 x 256 x 128 x 16 fp32 15.8 / 9.0;
 // 4 x 64 x 1024 x 16 fp32 12.4 / 9.6; 1 x 512 x 32 x 16 fp32 17.8 / 14.7;
 // 4 x 128 x 256 x 16 bf16 ZOH 17.2 / 8.5; but 1 x 1024 x 32 x 16 fp32
 // 19.6 / 27.2, 8 x 128 x 1024 x 16 fp32 ZOH 39.6 / 44.9 and
