@@ -248,8 +248,9 @@ size_t ssm_scan_workspace_size(const ssm_scan_args_t* args);
 
 /* Time steps per chunk the plan uses for these arguments (equal to seqlen
  * when the scan is not split).  Pure host function; 0 for invalid sizes.
- * With chunk_len = 0 and no conv prologue, short sequences of few channels
- * (seqlen <= 512 and batch * dim * ceil(seqlen / 64) <= 4096) run as one
+ * With chunk_len = 0, sequences of at most 32 steps are not split, and short
+ * sequences of few channels (seqlen <= 512 and batch * dim * ceil(seqlen /
+ * 64) <= min(4096, 64 * seqlen)) run as one
  * pass with the time steps across a wave's lanes, each block of 64 steps
  * solved by a parallel associative scan over the lanes (53ai.com explainer,
  * section 3.3); that plan reports seqlen and needs no workspace. */

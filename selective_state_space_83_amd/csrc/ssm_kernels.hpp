@@ -982,9 +982,10 @@ __device__ __forceinline__ void store_state(float* p, const float (&h)[NL]) {
 // slow-decay threshold (wave-uniform test), each decay is carried as a pair
 // a + r, with r the part of exp(Delta A) that rounding a lost
 // (exp_residual), and the product of two decays keeps its own rounding
-// error, fma(a, a', -a a'), in r.  No conv prologue (the plan routes conv to
-// the chunked passes); GATE multiplies y by silu(z); SAVE writes the state
-// entering every kSaveStride-th step to p.hsave.
+// error, fma(a, a', -a a'), in r.  CONV runs the causal conv prologue per
+// lane (each lane loads its step's three earlier inputs) and hands the last
+// conv_k - 1 inputs to p.cs_out; GATE multiplies y by silu(z); SAVE writes
+// the state entering every kSaveStride-th step to p.hsave.
 // One combine of the lane scan: every lane takes the pair of the lane CTRL
 // reaches (the identity where it reaches none) as the earlier operand.
 template <int CTRL, int ROWS>
@@ -1027,12 +1028,22 @@ __device__ __forceinline__ void wave_scan(float (&a)[N], float (&r)[N], float (&
   wave_combine<0x143, 0xC, RES>(a, r, bb);
 }
 
-template <int N, typename InT, typename OutT, int DISC, bool GATE, bool SAVE>
+template <int N, typename InT, typename OutT, int DISC, bool GATE, bool SAVE, bool CONV>
 __global__ void __launch_bounds__(kWave) k_scan_wave(const ScanParams p) {
   const int64_t wg = blockIdx.x;
   const int64_t D = p.D, L = p.L;
   const int64_t b = wg / D, d = wg - b * D;
   const int lane = threadIdx.x;
+  // conv prologue: the channel's taps (zero-padded at the oldest end) and
+  // the caller's window, x[t < 0] = win[S + t] (zero where there is none)
+  float cw[kConvTaps] = {0.f, 0.f, 0.f, 0.f};
+  float cb = 0.0f;
+  const int S = CONV ? p.conv_k - 1 : 0;
+  const float* win = (CONV && p.cs_in) ? p.cs_in + (b * D + d) * S : nullptr;
+  if constexpr (CONV) {
+    for (int k = 0; k < p.conv_k; ++k) cw[kConvTaps - p.conv_k + k] = p.conv_w[d * p.conv_k + k];
+    cb = p.conv_b ? p.conv_b[d] : 0.0f;
+  }
   ChanConst<N, DISC> cc;
   load_chan<N, DISC>(cc, p.A + d * N, p.exact_thr);
   const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
@@ -1052,6 +1063,19 @@ __global__ void __launch_bounds__(kWave) k_scan_wave(const ScanParams p) {
     const bool in = t < L;
     const int64_t tc = in ? t : L - 1;   // lanes past the end read the last step
     float u = ld(xp + tc * D);
+    if constexpr (CONV) {
+      // u = silu(bias + sum_k w[k] x[t - 3 + k]): the three earlier inputs
+      // from memory (their neighbours' rows, already in cache), or from the
+      // window before token 0
+      float z = fmaf(cw[3], u, cb);
+#pragma unroll
+      for (int k = 1; k <= 3; ++k) {
+        const int64_t tk = tc - k;
+        const float xk = tk >= 0 ? ld(xp + tk * D) : ((win && tk >= -S) ? win[S + tk] : 0.0f);
+        z = fmaf(cw[3 - k], xk, z);
+      }
+      u = silu(z);
+    }
     float dv = ld(dp + tc * D);
     if (dtm != kDtRaw) dv = dt_transform(dv, dtb, dtm);
     const float zv = GATE ? ld(zp + tc * D) : 0.0f;
@@ -1115,6 +1139,15 @@ __global__ void __launch_bounds__(kWave) k_scan_wave(const ScanParams p) {
 #pragma unroll
     for (int n = 0; n < N; ++n)
       hc[n] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h[n]), kWave - 1));
+  }
+  if constexpr (CONV) {
+    // the last S raw inputs, oldest first, reaching into the window when
+    // L < S: lane j < S writes x[L - S + j]
+    if (p.cs_out && lane < S) {
+      const int64_t tj = L - S + lane;
+      const float xj = tj >= 0 ? ld(xp + tj * D) : ((win && tj >= -S) ? win[S + tj] : 0.0f);
+      p.cs_out[(b * D + d) * S + lane] = xj;
+    }
   }
 }
 

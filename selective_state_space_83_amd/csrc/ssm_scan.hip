@@ -57,6 +57,12 @@ ssm_status_t fail(ssm_status_t s, const char* fmt, ...) {
 // 1 x 2^20 x 512 x 16 bf16 (whole scan): 2048-step chunks 2.87 ms, 1024
 // 2.61, 512 2.52, 256 2.50, 128 2.60; 4 x 8192 x 2560 x 16 bf16 with ZOH and
 // the conv: 328 steps 677 us, 256 steps 661 us.
+// Sequences of at most kNoSplitSteps steps are not cut at all: the summary
+// and carry launches cost more than a wave walking the few steps saves.
+// Measured, fp32, us per call back to back (one chunk / 8-step chunks):
+// 1 x 16 x 2048 x 16 6.6 / 11.6; 1 x 16 x 4096 x 16 with the conv 8.1 /
+// 13.5; 1 x 32 x 4096 x 16 10.7 / 12.7, with the conv 12.4 / 14.5.
+constexpr int64_t kNoSplitSteps = 32;
 constexpr int64_t kTargetWaves = 4096;
 constexpr int64_t kShortTargetWaves = 3072;
 constexpr int64_t kShortChunk = 64;
@@ -141,6 +147,7 @@ Plan make_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t chunk_len) {
     };
     int64_t C = chunks(kTargetWaves);
     if (C > 1 && (L + C - 1) / C < kShortChunk) C = chunks(kShortTargetWaves);
+    if (L <= kNoSplitSteps) C = 1;
     T = (L + C - 1) / C;
     if (C > 1) T = (T + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
     if (C >= kBalanceChunks) T = std::min(T, kLongChunk);
@@ -161,13 +168,18 @@ Plan make_plan(int64_t Bt, int64_t L, int64_t D, int64_t N, int32_t chunk_len) {
 
 // Whether a problem takes the one-pass lane scan (k_scan_wave: time steps
 // across a wave's lanes, one wave per channel, a DPP scan per block of 64
-// steps): no conv prologue (the chunked passes carry its window), no forced
-// chunk length, and a short sequence of few channels.  A block's six
+// steps, the conv prologue per lane): no forced chunk length, and a short
+// sequence of few channels.  A block's six
 // dependent combines take about 1.5 us alone on a SIMD, and every element
 // costs about six combines of work instead of one recurrence step, so it
 // wins where the chunked plan's three launches and its waves' first-step
 // latencies dominate: at most 8 blocks (seqlen <= 512) and at most 4096
-// wave-blocks (batch * dim * ceil(seqlen / 64)).  Measured, us per call
+// wave-blocks (batch * dim * ceil(seqlen / 64)), or 64 * seqlen of them for
+// sequences shorter than a block, whose lanes stand partly idle while the
+// chunked plan walks the few steps in one chunk (fp32, us per call, lane
+// scan / one chunk: 1 x 8 x 256 x 16 6.2 / 6.3, 1 x 8 x 2048 x 16 7.5 /
+// 6.2, 1 x 16 x 2048 x 16 7.6 / 6.6, 1 x 32 x 2048 x 16 8.1 / 10.6,
+// 2 x 32 x 2048 x 16 12.3 / 10.7, with the conv alike).  Measured, us per call
 // back to back (chunked passes / lane scan): 1 x 128 x 256 x 16 bf16
 // 14.8 / 6.0; 2 x 256 x 128 x 16 fp32 15.8 / 9.0;
 // 4 x 64 x 1024 x 16 fp32 12.4 / 9.6; 1 x 512 x 32 x 16 fp32 17.8 / 14.7;
@@ -178,12 +190,12 @@ constexpr int64_t kWaveMaxSteps = 512;
 constexpr int64_t kWaveMaxBlocks = 4096;
 bool wave_wins(int64_t Bt, int64_t L, int64_t D) {
   const int64_t blocks = (L + ssmk::kWave - 1) / ssmk::kWave;
-  return L <= kWaveMaxSteps && Bt * D <= kWaveMaxBlocks / blocks;
+  return L <= kWaveMaxSteps && Bt * D <= std::min(kWaveMaxBlocks, ssmk::kWave * L) / blocks;
 }
 
 Plan one_pass_plan(const ssm_scan_args_t* a, const Plan& chunked) {
   const int64_t L = a->seqlen, D = a->dim;
-  if (a->conv_w || a->chunk_len > 0 || L == 0 || a->batch * D == 0) return chunked;
+  if (a->chunk_len > 0 || L == 0 || a->batch * D == 0) return chunked;
   if (!wave_wins(a->batch, L, D)) return chunked;
   Plan pl;
   pl.wave = true;
@@ -473,20 +485,18 @@ ssm_status_t launch_combine(ssmk::ScanParams kp, const Grouping& grp, hipStream_
 template <int N, typename InT, typename OutT, int DISC, bool CONV, bool GATE>
 ssm_status_t run_scan(ssmk::ScanParams kp, const Plan& pl, hipStream_t s, hipEvent_t ev0,
                       hipEvent_t ev1) {
-  if constexpr (!CONV) {
-    if (pl.wave) {
-      kp.nwg = int32_t(kp.Bt * kp.D);
-      if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return fail(SSM_ERR_HIP, "hipEventRecord failed");
-      if (kp.hsave)
-        hipLaunchKernelGGL((ssmk::k_scan_wave<N, InT, OutT, DISC, GATE, true>), dim3(kp.nwg),
-                           dim3(ssmk::kWave), 0, s, kp);
-      else
-        hipLaunchKernelGGL((ssmk::k_scan_wave<N, InT, OutT, DISC, GATE, false>), dim3(kp.nwg),
-                           dim3(ssmk::kWave), 0, s, kp);
-      if (ssm_status_t st = launch_status("k_scan_wave")) return st;
-      if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return fail(SSM_ERR_HIP, "hipEventRecord failed");
-      return SSM_OK;
-    }
+  if (pl.wave) {
+    kp.nwg = int32_t(kp.Bt * kp.D);
+    if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return fail(SSM_ERR_HIP, "hipEventRecord failed");
+    if (kp.hsave)
+      hipLaunchKernelGGL((ssmk::k_scan_wave<N, InT, OutT, DISC, GATE, true, CONV>), dim3(kp.nwg),
+                         dim3(ssmk::kWave), 0, s, kp);
+    else
+      hipLaunchKernelGGL((ssmk::k_scan_wave<N, InT, OutT, DISC, GATE, false, CONV>), dim3(kp.nwg),
+                         dim3(ssmk::kWave), 0, s, kp);
+    if (ssm_status_t st = launch_status("k_scan_wave")) return st;
+    if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return fail(SSM_ERR_HIP, "hipEventRecord failed");
+    return SSM_OK;
   }
   if (pl.C > 1) {
     kp.nwg = int32_t(kp.Bt * (pl.C - 1) * pl.dtiles);

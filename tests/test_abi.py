@@ -462,10 +462,11 @@ def test_auto_plan(lib, shape, T):
 
 def test_single_pass_plan_rule(lib):
     """Short sequences of few channels (seqlen <= 512 and batch * dim *
-    ceil(seqlen / 64) <= 4096 blocks of 64 steps) take the one-pass lane
-    scan: the plan reports seqlen and needs no workspace.  A forced chunk
-    length, a conv prologue, a longer sequence or more channels keep the
-    chunked passes."""
+    ceil(seqlen / 64) <= 4096 blocks of 64 steps, fewer below 64 steps) take
+    the one-pass lane
+    scan: the plan reports seqlen and needs no workspace, with or without
+    the conv prologue.  A forced chunk length, a longer sequence or more
+    channels keep the chunked passes."""
     assert plan(lib, batch=2, L=64, D=32, N=16) == (64, 0)            # 64 blocks
     assert plan(lib, batch=4, L=64, D=1024, N=16) == (64, 0)          # 4096 blocks
     assert plan(lib, batch=1, L=512, D=512, N=16) == (512, 0)         # 8 x 512
@@ -479,10 +480,33 @@ def test_single_pass_plan_rule(lib):
     assert T < 65 and ws > 0
     T, ws = plan(lib, batch=2, L=64, D=128, N=16, chunk_len=8)
     assert T == 8 and ws > 0
+    # the conv prologue runs inside the lane scan too
     a = valid_scan_args(batch=2, L=64, D=128, N=16)
     a.conv_w, a.conv_k = 0x100000000 + 12 * GB, 4
-    assert lib.ssm_scan_plan_chunk_len(ctypes.byref(a)) < 64
+    assert lib.ssm_scan_plan_chunk_len(ctypes.byref(a)) == 64
+    assert lib.ssm_scan_workspace_size(ctypes.byref(a)) == 0
+    a = valid_scan_args(batch=2, L=1000, D=128, N=16)
+    a.conv_w, a.conv_k = 0x100000000 + 12 * GB, 4
+    assert lib.ssm_scan_plan_chunk_len(ctypes.byref(a)) < 1000
     assert lib.ssm_scan_workspace_size(ctypes.byref(a)) > 0
+
+
+def test_short_sequence_rules(lib):
+    """Shorter than a block of 64 steps, at most 64 * seqlen wave-blocks take
+    the lane scan (its lanes stand partly idle); sequences of at most 32 steps
+    are never cut into chunks."""
+    a = lambda **kw: lane_scan(lib, N=16, **kw)
+    assert a(batch=1, L=8, D=256) == 1          # 256 <= 512
+    assert a(batch=1, L=8, D=2048) == 0         # 2048 > 512
+    assert a(batch=1, L=32, D=2048) == 1        # 2048 <= 2048
+    assert a(batch=2, L=32, D=2048) == 0
+    assert a(batch=1, L=1, D=64) == 1
+    assert a(batch=1, L=1, D=65) == 0
+    assert plan(lib, batch=1, L=16, D=2048, N=16) == (16, 0)
+    assert plan(lib, batch=2, L=32, D=2048, N=16) == (32, 0)
+    assert plan(lib, batch=1, L=1, D=65, N=16) == (1, 0)
+    T, ws = plan(lib, batch=2, L=33, D=2048, N=16)
+    assert T < 33 and ws > 0
 
 
 def lane_scan(lib, **kw):
@@ -493,8 +517,8 @@ def lane_scan(lib, **kw):
 def test_lane_scan_query(lib):
     """ssm_scan_plan_lane_scan tells the one-pass lane scan from the chunked
     passes, also where both report seqlen and no workspace (a chunked plan of
-    one chunk), and reads 0 for a conv prologue, a forced chunk length and
-    invalid sizes."""
+    one chunk); a conv prologue keeps the lane scan; it reads 0 for a forced
+    chunk length and invalid sizes."""
     assert lane_scan(lib, batch=2, L=64, D=32, N=16) == 1
     assert lane_scan(lib, batch=1, L=512, D=512, N=16) == 1
     assert lane_scan(lib, batch=5, L=64, D=1024, N=16) == 0
@@ -505,7 +529,7 @@ def test_lane_scan_query(lib):
     assert lane_scan(lib, batch=256, L=4, D=5120, N=16) == 0
     a = valid_scan_args(batch=2, L=64, D=128, N=16)
     a.conv_w, a.conv_k = 0x100000000 + 12 * GB, 4
-    assert lib.ssm_scan_plan_lane_scan(ctypes.byref(a)) == 0
+    assert lib.ssm_scan_plan_lane_scan(ctypes.byref(a)) == 1
     a = valid_scan_args(batch=2, L=64, D=32, N=16)
     a.dstate = 0
     assert lib.ssm_scan_plan_lane_scan(ctypes.byref(a)) == 0
